@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X WKV-6 forward (tokens/s = B*T per second).
+
+One step = one wkv6_fwd call (the whole hot path: load, decay transform,
+in-chunk scans, MFMA contractions, state carries in both directions, merge and
+store) over one batch of synthetic input already resident in HBM.  Inputs and
+outputs rotate over enough copies that no step finds its data in the 256 MB
+Infinity Cache left by the previous steps.
+
+Prints ONE JSON line (rank 0) with, besides the throughput:
+  roofline      achieved HBM bandwidth of the forward kernel(s) from HIP events
+                on the launch stream: algorithmic bytes per call / mean call time
+  mfma          executed matrix-core work per call and its rate vs the bf16 peak
+  cpu_baseline  the float64 CPU oracle timed on the host on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from linear_attention_rnn_amd import inputs as I  # noqa: E402
+
+HEADLINE = "image-base-bidir-bf16"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+MALL_BYTES = 256 << 20
+MFMA_FLOPS = 2 * 16 * 16 * 32  # one v_mfma_f32_16x16x32_bf16
+METRIC = "WKV6 fwd tokens/s (B·T/s) + % HBM roofline & MFMA util at N=64, 1 GPU"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_rnn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def mfma_count(w: I.Workload) -> int:
+    """v_mfma_f32_16x16x32_bf16 instructions one call issues (mirrors the
+    kernels' loop structure)."""
+    L = 64
+    nc = math.ceil(w.T / L)
+    bidir = w.mode == "bidirectional"
+    vsplit = 3 if w.dtype == "f32" else 2   # products with the value tile
+    per_bh = 0
+    for ch in range(nc):
+        lv = min(L, w.T - ch * L)
+        for wave in range(4):
+            if 16 * wave >= lv:
+                continue
+            tiles = (wave + 1) + ((4 - wave) if bidir else 0)
+            per_bh += tiles * 2 * 3                                  # in-chunk scores
+            ksteps = 2 if bidir else (1 if wave < 2 else 2)
+            per_bh += ksteps * 4 * vsplit                            # scores x V
+            if ch > 0:
+                per_bh += 2 * 4 * 3                                  # left state
+            if bidir and ch < nc - 1:
+                per_bh += 2 * 4 * 3                                  # right state
+        if ch < nc - 1:
+            per_bh += 4 * 2 * 4 * vsplit                             # state update
+        if bidir and ch >= 1:
+            per_bh += 4 * 2 * 4 * vsplit                             # reverse sweep
+    return per_bh * w.B * w.H
+
+
+def traffic_record(workload: str):
+    """HBM bytes per call from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def cpu_baseline(w: I.Workload, x: dict, budget_s: float = 20.0) -> dict:
+    """Time the float64 oracle on whole batch items of the same workload until
+    about `budget_s` seconds of CPU work, single-threaded."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import wkv6_ref
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        wkv6_ref(x["r"][:1], x["k"][:1], x["v"][:1], x["w_raw"][:1], x["u"], w.H, w.mode)
+        t1 = time.perf_counter() - t0
+        nb = max(1, min(w.B, int(budget_s / max(t1, 1e-3))))
+        if nb > 1:
+            t0 = time.perf_counter()
+            wkv6_ref(x["r"][:nb], x["k"][:nb], x["v"][:nb], x["w_raw"][:nb], x["u"], w.H, w.mode)
+            el = time.perf_counter() - t0
+        else:
+            el = t1
+    return {"value": nb * w.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nb} of {w.B} batch items (T={w.T}, C={w.C}, H={w.H}, {w.mode}, "
+                      f"float64 numpy recurrence, BLAS limited to 1 thread), {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=[x.name for x in I.WORKLOADS])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="reuse one input set (warm Infinity Cache; not the headline number)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from linear_attention_rnn_amd import wkv6
+
+    def device_inputs(xs, dtype):
+        out = []
+        for key in ("r", "k", "v", "w_raw"):
+            a = xs[key]
+            if dtype == "bf16":
+                out.append(torch.from_numpy(I.bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda())
+            else:
+                out.append(torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda())
+        out.append(torch.from_numpy(np.ascontiguousarray(xs["u"], np.float32)).cuda())
+        return out
+
+    w = I.workload(args.workload)
+    x = I.make_inputs(w)
+    per_copy = w.algorithmic_bytes()
+    ncopy = 1 if args.no_rotate else max(2, math.ceil(2 * MALL_BYTES / per_copy) + 1)
+    sets = []
+    for _ in range(ncopy):
+        d = device_inputs(x, w.dtype)
+        y = torch.empty((w.B, w.T, w.C), dtype=torch.float32, device="cuda")
+        sets.append((d, y))
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(i):
+        d, y = sets[i % ncopy]
+        wkv6.fwd(*d, w.H, w.mode, out=y, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_ms = float(np.mean(per_call_ms))
+    ms_per_step = 1e3 * wall / args.steps
+
+    alg_bytes = per_copy
+    achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
+    n_mfma = mfma_count(w)
+    mfma_tflops = n_mfma * MFMA_FLOPS / (mean_ms * 1e-3) / 1e12
+    traffic = traffic_record(w.name)
+
+    out = {
+        "metric": METRIC,
+        "value": w.tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded numpy draws, recipe in linear_attention_rnn_amd/inputs.py)",
+        "config": {"workload": w.name, "mode": w.mode, "B": w.B, "T": w.T, "C": w.C, "H": w.H,
+                   "N": w.N, "inputs": w.dtype, "state_and_output": "f32",
+                   "rotating_copies": ncopy, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "wkv6 forward call (reverse-state + forward kernels)",
+                     "mean_call_ms": mean_ms, "algorithmic_bytes": alg_bytes},
+        "mfma": {"instructions": n_mfma, "executed_tflops": mfma_tflops,
+                 "util": mfma_tflops / MFMA_BF16_PEAK_TFLOPS, "peak_tflops": MFMA_BF16_PEAK_TFLOPS},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

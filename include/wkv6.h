@@ -1,0 +1,111 @@
+/*
+ * wkv6.h -- C ABI of the MI355X (gfx950) RWKV-6 WKV forward operator.
+ *
+ * What the operator computes (the WKV-6 forward of the deepglint/rwkv-clip
+ * pages: "How Custom CUDA Kernels (wkv6_cuda.cu) Implement the WKV Operation",
+ * section "Forward Pass Implementation in kernel_forward", and "RWKV
+ * Architecture" on llms.blog, sections "RWKV-5 Eagle" and "RWKV-6 Finch"):
+ *
+ *   For every batch item b and head h (head h owns channels [64h, 64h+64) of
+ *   the [B, T, C] tensors, C = 64*H), with the per-token, per-channel decay
+ *   w_t[c] = exp(-exp(w_raw_t[c])) and a 64x64 fp32 state S (rows: key /
+ *   receptance channel c, columns: value channel n) starting at zero:
+ *
+ *     y_t[n] = sum_c r_t[c] * ( S[c][n] + u[c] * k_t[c] * v_t[n] )
+ *     S[c][n] <- w_t[c] * S[c][n] + k_t[c] * v_t[n]
+ *
+ *   i.e. token i < t reaches t with weight prod_{i<j<t} w_j and token t
+ *   itself with weight u.  Bidirectional mode adds, from a second zero state
+ *   swept from the last token to the first, the strictly later tokens:
+ *
+ *     y_t[n] += sum_c r_t[c] * sum_{i>t} (prod_{t<j<i} w_j[c]) k_i[c] v_i[n]
+ *
+ *   (u is applied once; the wrapper on the "What is the WKV mechanism" page,
+ *   section "CUDA Wrapper (Image Side)", supplies the decay as minus the
+ *   exponential of w, which the kernel exponentiates again; here the library
+ *   takes w_raw itself and applies both exponentials on the GPU.)
+ *
+ * All arithmetic runs in the library's HIP kernels.  The kernels evaluate the
+ * definition in chunks of 64 tokens with matrix-core (MFMA) contractions on
+ * split bf16 operands (each fp32 operand carried as a high and a low bf16
+ * part) and fp32 accumulation; results agree with an exact evaluation to
+ * about 1e-4 of the output's rms (see the tests for the bounds checked).
+ */
+#ifndef WKV6_H
+#define WKV6_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WKV6_ABI_VERSION 1
+
+/* mode */
+#define WKV6_MODE_CAUSAL        0
+#define WKV6_MODE_BIDIRECTIONAL 1
+
+/* dtype of r, k, v, w_raw (u and y are always float32) */
+#define WKV6_DTYPE_F32  0
+#define WKV6_DTYPE_BF16 1
+
+/* status codes */
+#define WKV6_OK               0  /* success; also B == 0 or T == 0 (nothing done) */
+#define WKV6_ERR_INVALID_ARG  1  /* negative size, H < 1, C % H != 0, null pointer,
+                                    unknown mode/dtype, y overlapping an input */
+#define WKV6_ERR_UNSUPPORTED  2  /* head size C / H other than 64, or a size whose
+                                    index arithmetic would overflow */
+#define WKV6_ERR_MISALIGNED   3  /* a pointer not aligned to 16 bytes */
+#define WKV6_ERR_HIP          4  /* a HIP runtime error (launch, allocation) */
+
+/*
+ * wkv6_fwd -- enqueue one WKV-6 forward on `stream`.
+ *
+ *   B, T, C, H    batch, tokens, channels, heads; C must equal 64 * H.
+ *   r, k, v,      device pointers to contiguous row-major [B, T, C] tensors of
+ *   w_raw         `dtype` (float32, or bfloat16 stored as 16-bit words).
+ *                 w_raw is the pre-transform decay: w = exp(-exp(w_raw)).
+ *                 Supported w_raw: finite values up to 1.5 (w >= 0.011), or
+ *                 -inf (w = 1).  Larger values can overflow the in-chunk
+ *                 decay factors; +inf and NaN are not supported.
+ *   u             device pointer to C float32 values, laid out [H, 64].
+ *   y             device pointer to a [B, T, C] float32 output.  Fully
+ *                 overwritten (never accumulated into); must not overlap any
+ *                 input.
+ *   mode          WKV6_MODE_CAUSAL or WKV6_MODE_BIDIRECTIONAL.
+ *   dtype         WKV6_DTYPE_F32 or WKV6_DTYPE_BF16.
+ *   stream        a hipStream_t passed as void* (NULL = the null stream).
+ *
+ * Ownership: every pointer is caller-owned device memory; the library keeps
+ * none of them after returning.  Bidirectional calls with T > 64 take a
+ * temporary device workspace of B*H*(ceil(T/64)-1)*16 KiB, allocated and
+ * released in stream order (hipMallocAsync / hipFreeAsync on `stream`).
+ *
+ * Execution: asynchronous on `stream`; the call does not synchronise the
+ * host.  The caller keeps the buffers alive until the stream has run the
+ * work.  Calls are thread-safe; the only library state is a per-thread last
+ * error message (wkv6_last_error).
+ *
+ * Errors: returns a WKV6_* status.  On INVALID_ARG, UNSUPPORTED and
+ * MISALIGNED nothing is enqueued.  Input values are not checked: NaN and Inf
+ * propagate to y.
+ */
+int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H,
+             const void* r, const void* k, const void* v, const void* w_raw,
+             const float* u, float* y, int mode, int dtype, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* wkv6_status_str(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* wkv6_last_error(void);
+
+/* WKV6_ABI_VERSION of the loaded library. */
+int wkv6_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV6_H */

@@ -1,0 +1,112 @@
+// C ABI of the WKV-6 forward library: argument checks, workspace, launch.
+// The declarations and their contract live in include/wkv6.h.
+#include "wkv6.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "wkv6_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv6_abi_version(void) { return WKV6_ABI_VERSION; }
+
+const char* wkv6_status_str(int status) {
+  switch (status) {
+    case WKV6_OK: return "ok";
+    case WKV6_ERR_INVALID_ARG: return "invalid argument";
+    case WKV6_ERR_UNSUPPORTED: return "unsupported size";
+    case WKV6_ERR_MISALIGNED: return "misaligned pointer";
+    case WKV6_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* wkv6_last_error(void) { return g_last_error.c_str(); }
+
+int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k,
+             const void* v, const void* w_raw, const float* u, float* y, int mode, int dtype,
+             void* stream) {
+  g_last_error.clear();
+  if (B < 0 || T < 0 || C < 0 || H < 1)
+    return fail(WKV6_ERR_INVALID_ARG, "sizes must be B, T, C >= 0 and H >= 1");
+  if (C % H != 0) return fail(WKV6_ERR_INVALID_ARG, "C must be a multiple of H");
+  if (mode != WKV6_MODE_CAUSAL && mode != WKV6_MODE_BIDIRECTIONAL)
+    return fail(WKV6_ERR_INVALID_ARG, "unknown mode");
+  if (dtype != WKV6_DTYPE_F32 && dtype != WKV6_DTYPE_BF16)
+    return fail(WKV6_ERR_INVALID_ARG, "unknown dtype");
+  if (C / H != wkv6::kHead) return fail(WKV6_ERR_UNSUPPORTED, "head size C/H must be 64");
+  if (B == 0 || T == 0) return WKV6_OK;
+  if (T > INT_MAX - wkv6::kChunk || B * H > INT_MAX || B > INT64_MAX / T || B * T > INT64_MAX / (4 * C))
+    return fail(WKV6_ERR_UNSUPPORTED, "sizes exceed the supported index range");
+  const void* ptrs[6] = {r, k, v, w_raw, u, y};
+  const char* names[6] = {"r", "k", "v", "w_raw", "u", "y"};
+  for (int i = 0; i < 6; ++i) {
+    if (!ptrs[i]) return fail(WKV6_ERR_INVALID_ARG, std::string("null pointer: ") + names[i]);
+  }
+  for (int i = 0; i < 6; ++i) {
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16)
+      return fail(WKV6_ERR_MISALIGNED, std::string("pointer not 16-byte aligned: ") + names[i]);
+  }
+  const size_t elems = (size_t)B * (size_t)T * (size_t)C;
+  const size_t isz = dtype == WKV6_DTYPE_BF16 ? 2 : 4;
+  const size_t ybytes = elems * 4;
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(y, ybytes, ptrs[i], elems * isz))
+      return fail(WKV6_ERR_INVALID_ARG, std::string("y overlaps ") + names[i]);
+  }
+  if (overlaps(y, ybytes, u, (size_t)C * 4)) return fail(WKV6_ERR_INVALID_ARG, "y overlaps u");
+
+  wkv6::FwdArgs a;
+  a.B = B;
+  a.T = T;
+  a.C = C;
+  a.H = H;
+  a.r = r;
+  a.k = k;
+  a.v = v;
+  a.w_raw = w_raw;
+  a.u = u;
+  a.y = y;
+  a.bidirectional = mode == WKV6_MODE_BIDIRECTIONAL;
+  a.bf16 = dtype == WKV6_DTYPE_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const size_t ws_bytes = wkv6::workspace_bytes(a);
+  void* ws = nullptr;
+  if (ws_bytes) {
+    const hipError_t e = hipMallocAsync(&ws, ws_bytes, s);
+    if (e != hipSuccess)
+      return fail(WKV6_ERR_HIP, std::string("workspace allocation: ") + hipGetErrorString(e));
+  }
+  const hipError_t e = wkv6::enqueue_fwd(a, ws, s);
+  if (ws) {
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e == hipSuccess && ef != hipSuccess)
+      return fail(WKV6_ERR_HIP, std::string("workspace release: ") + hipGetErrorString(ef));
+  }
+  if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return WKV6_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Internal interface between the C ABI layer (wkv6_api.cpp) and the HIP
+// kernels (wkv6_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv6 {
+
+// Head size and chunk length the kernels are built for.
+constexpr int kHead = 64;
+constexpr int kChunk = 64;
+
+struct FwdArgs {
+  int64_t B, T, C, H;
+  const void* r;
+  const void* k;
+  const void* v;
+  const void* w_raw;
+  const float* u;
+  float* y;
+  bool bidirectional;
+  bool bf16;
+};
+
+// Bytes of device workspace a call needs (0 when none).
+size_t workspace_bytes(const FwdArgs& a);
+
+// Enqueue the kernels on `stream`.  `workspace` must hold workspace_bytes(a)
+// bytes (or be null when that is 0).  Returns the first HIP error, if any.
+hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream);
+
+}  // namespace wkv6

@@ -1,0 +1,126 @@
+"""ctypes binding of libwkv6.so (C ABI in include/wkv6.h).
+
+Argument marshalling only: every step of the WKV-6 forward runs in the
+library's HIP kernels.  PyTorch provides device memory and the current HIP
+stream.  There is no fallback: if the library is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libwkv6.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "wkv6.h")
+
+MODE_CAUSAL = 0
+MODE_BIDIRECTIONAL = 1
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_UNSUPPORTED = 2
+ERR_MISALIGNED = 3
+ERR_HIP = 4
+
+_MODES = {"causal": MODE_CAUSAL, "bidirectional": MODE_BIDIRECTIONAL}
+
+_lib = None
+
+
+class WKV6Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"wkv6_fwd failed with status {status}: {message}")
+        self.status = status
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/wkv6.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(wkv6_\w+)\s*\(", text, flags=re.M)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libwkv6.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing; build it with `python -m linear_attention_rnn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        L.wkv6_fwd.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                               ctypes.c_int, ctypes.c_int, vp]
+        L.wkv6_fwd.restype = ctypes.c_int
+        L.wkv6_status_str.argtypes = [ctypes.c_int]
+        L.wkv6_status_str.restype = ctypes.c_char_p
+        L.wkv6_last_error.argtypes = []
+        L.wkv6_last_error.restype = ctypes.c_char_p
+        L.wkv6_abi_version.argtypes = []
+        L.wkv6_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().wkv6_abi_version()
+
+
+def status_str(status: int) -> str:
+    return lib().wkv6_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib().wkv6_last_error().decode()
+
+
+def fwd_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, u: int,
+            y: int, mode: int, dtype: int, stream: int = 0) -> int:
+    """Direct call with integer addresses; returns the status code."""
+    return lib().wkv6_fwd(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype, stream)
+
+
+def fwd(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
+    """y = WKV6(r, k, v, w_raw, u) on the GPU.
+
+    r, k, v, w_raw: contiguous CUDA tensors [B, T, C] of one dtype (float32 or
+    bfloat16); u: contiguous float32 [C]; returns (or fills ``out``) a float32
+    [B, T, C] tensor.  Runs on ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    if r.dim() != 3:
+        raise ValueError("r must be [B, T, C]")
+    B, T, C = r.shape
+    for name, t in (("k", k), ("v", v), ("w_raw", w_raw)):
+        if t.shape != r.shape or t.dtype != r.dtype:
+            raise ValueError(f"{name} must match r in shape and dtype")
+    if r.dtype == torch.float32:
+        dtype = DTYPE_F32
+    elif r.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    else:
+        raise ValueError("r, k, v, w_raw must be float32 or bfloat16")
+    if u.dtype != torch.float32 or u.numel() != C:
+        raise ValueError("u must be float32 with C elements")
+    for name, t in (("r", r), ("k", k), ("v", v), ("w_raw", w_raw), ("u", u)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
+    elif out.shape != (B, T, C) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(r.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = fwd_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
+                 u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, handle)
+    if st != OK:
+        raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
+    return out

@@ -1,0 +1,84 @@
+"""The C ABI library loads and exports what include/wkv6.h declares; argument
+checks that return before any GPU work behave as documented.  No compute
+call is made here, so this runs without a GPU (it needs the built library,
+which __graft_entry__.build() or `python -m linear_attention_rnn_amd.build`
+produces)."""
+import ctypes
+import os
+
+import pytest
+
+from linear_attention_rnn_amd import wkv6
+
+pytestmark = pytest.mark.skipif(not os.path.exists(wkv6.LIB_PATH),
+                                reason="libwkv6.so not built")
+
+A = 0x10000  # fake, 16-byte aligned addresses: never dereferenced by these calls
+
+
+def test_exports_every_declared_function():
+    names = wkv6.header_functions()
+    assert set(names) == {"wkv6_fwd", "wkv6_status_str", "wkv6_last_error", "wkv6_abi_version"}
+    L = wkv6.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings():
+    assert wkv6.abi_version() == 1
+    assert wkv6.status_str(0) == "ok"
+    texts = {wkv6.status_str(s) for s in range(5)}
+    assert len(texts) == 5
+    assert wkv6.status_str(99) == "unknown status"
+
+
+def _call(B=2, T=8, C=128, H=2, ptrs=None, mode=0, dtype=0):
+    p = ptrs or [A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000]
+    return wkv6.fwd_raw(B, T, C, H, *p, mode, dtype, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), wkv6.ERR_INVALID_ARG),
+    (dict(T=-3), wkv6.ERR_INVALID_ARG),
+    (dict(C=-64), wkv6.ERR_INVALID_ARG),
+    (dict(H=0), wkv6.ERR_INVALID_ARG),
+    (dict(C=130, H=4), wkv6.ERR_INVALID_ARG),     # C not a multiple of H
+    (dict(mode=2), wkv6.ERR_INVALID_ARG),
+    (dict(dtype=5), wkv6.ERR_INVALID_ARG),
+    (dict(C=96, H=2), wkv6.ERR_UNSUPPORTED),      # head size 48
+    (dict(C=256, H=2), wkv6.ERR_UNSUPPORTED),     # head size 128
+    (dict(T=2 ** 31), wkv6.ERR_UNSUPPORTED),
+])
+def test_rejects_bad_arguments(kw, status):
+    assert _call(**kw) == status
+    assert wkv6.last_error() != ""
+
+
+def test_empty_problem_is_a_noop():
+    assert _call(B=0, ptrs=[0] * 6) == wkv6.OK
+    assert _call(T=0, ptrs=[0] * 6) == wkv6.OK
+    assert wkv6.last_error() == ""
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_null_pointer(which):
+    p = [A + 0x100000 * i for i in range(6)]
+    p[which] = 0
+    assert _call(ptrs=p) == wkv6.ERR_INVALID_ARG
+    assert "null" in wkv6.last_error()
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_misaligned_pointer(which):
+    p = [A + 0x100000 * i for i in range(6)]
+    p[which] += 4
+    assert _call(ptrs=p) == wkv6.ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_output_overlapping_an_input(which):
+    p = [A + 0x100000 * i for i in range(6)]
+    p[5] = p[which] + 16
+    assert _call(ptrs=p) == wkv6.ERR_INVALID_ARG
+    assert "overlaps" in wkv6.last_error()
