@@ -394,9 +394,22 @@ __device__ __forceinline__ void block_end8(const float* sBT, int I, int cb, floa
   }
 }
 
+// Prefix at the end of token block I (E_I) for one channel, summed in the
+// order block_sums uses.
+__device__ __forceinline__ float block_end(const float* sBT, int I, int c) {
+  float o = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    if (jj <= I) o += sBT[jj * 64 + c];
+  return o;
+}
+
 // ---------------------------------------------------------------------------
 // Segment pre-pass: one workgroup per (batch, head, segment); sweeps the
-// segment's chunks from last to first.
+// segment's chunks from last to first.  The state each chunk receives from
+// the later chunks of its segment is stored split, multiplied by the chunk's
+// own total decay 2^Ltot when the chunk takes the fast path (the forward
+// kernel then pairs it with the query r 2^(-Lin)), unscaled otherwise.
 template <bool BF16, bool BIDIR, bool CARRY>
 __global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
   constexpr int SP = BF16 ? 2 : 3;
@@ -441,8 +454,10 @@ __global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
     const bool valid = (int64_t)ch * LC + tau < T;
     lds_barrier();
     fetch(max(ch - 1, c0), nxt);
+    if ((int64_t)ch * LC + LC > T) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) mask_row<BF16>(cur[i], valid);
+      for (int i = 0; i < 3; ++i) mask_row<BF16>(cur[i], valid);
+    }
     float lin[2][8];
     block_scan<BF16>(cur[2], valid, lin);
     publish_block_totals(lin, sBT, J, g, li);
@@ -455,6 +470,7 @@ __global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
         for (int j = 0; j < 8; ++j) lds_write1<SV>(sV, 32 * ks + 8 * g + j, tau, v[ks][j]);
     }
     lds_barrier();
+    bool slow = false;
     {
       float k[2][8];
       unpack<BF16>(cur[0], k);
@@ -465,6 +481,7 @@ __global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int c = 32 * ks + 8 * g + j;
+          slow |= tot[j] < -kSpanMax;
           const float lin_c = lin[ks][j] + off[j];
           const float lex_c = row_shr<1>(lin[ks][j]) + off[j];
           if (BIDIR) lds_write1<SP>(sEb, c, tau, k[ks][j] * ex2(lex_c));
@@ -476,22 +493,25 @@ __global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
         }
       }
     }
+    slow = __any(slow);   // every wave sees all 64 channels: uniform in the workgroup
     lds_barrier();
 
+    float dec[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dec[j] = ex2(sTot[16 * J + 4 * g + j]);
     // state each chunk receives from the later chunks of the segment
     if (BIDIR && ch < c1 - 1) {
       __bf16* dst = p.rev + ((int64_t)bh * p.NC + ch) * (SP * PL);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const float x[4] = {Sb[nt][0], Sb[nt][1], Sb[nt][2], Sb[nt][3]};
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = slow ? Sb[nt][j] : Sb[nt][j] * dec[j];
         gl_write4<SP>(dst, 16 * nt + li, 16 * J + 4 * g, x);
       }
     }
     // Sb <- 2^Ltot Sb + (k 2^Lex)^T V ;  F += (k 2^(Ltot - Lin + D))^T V
     if (BIDIR) {
-      float dec[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dec[j] = ex2(sTot[16 * J + 4 * g + j]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -536,6 +556,29 @@ __global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
   }
 }
 
+// Column read of a split plane set: k-slots j = 0..7 are rows r0 + j of
+// column col (an A operand whose K dimension runs down the stored rows).
+template <int S>
+__device__ __forceinline__ Op<S> lds_read_col8(const __bf16* P, int r0, int col) {
+  Op<S> o;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o.p[s][j] = P[s * PL + swz(r0 + j, col)];
+  return o;
+}
+
+template <int S>
+__device__ __forceinline__ void join8(const Op<S>& o, float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v = 0.f;
+#pragma unroll
+    for (int s = S - 1; s >= 0; --s) v += (float)o.p[s][j];
+    x[j] = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Main sweep: outputs of one segment, left to right.
 template <bool BF16, bool BIDIR, bool CARRY>
@@ -545,7 +588,6 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
   constexpr bool RIN = BIDIR && CARRY;
   __shared__ __attribute__((aligned(16))) __bf16 sKf[SP * PL];              // keys, past tokens [i][c]
   __shared__ __attribute__((aligned(16))) __bf16 sKb[BIDIR ? SP * PL : 8];  // keys, later tokens [i][c]
-  __shared__ __attribute__((aligned(16))) __bf16 sKt[SP * PL];              // keys of the state update [c][i]
   __shared__ __attribute__((aligned(16))) __bf16 sV[SV * PL];               // V^T [n][t]
   __shared__ __attribute__((aligned(16))) __bf16 sS[SP * PL];               // S^T [n][c]
   __shared__ __attribute__((aligned(16))) __bf16 sSr[BIDIR ? SP * PL : 8];  // S'^T [n][c] entering this chunk
@@ -572,7 +614,7 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
   for (int nt = 0; nt < 4; ++nt) S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // State from the later segments, for the staging elements of this thread
   // (row tid / 4, columns 16 (tid % 4) .. + 15 of S'^T), and the log2 decay
-  // from the current chunk's end to the end of this segment for those columns.
+  // from the current chunk's start to the end of this segment for those columns.
   float Rr[16], rf[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) Rr[j] = rf[j] = 0.f;
@@ -614,11 +656,12 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
     }
   }
 
-  // Per-chunk global data, double-buffered: [0] r, [1] k, [2] v, [3] w rows of
-  // the lane's home token, and 2 SP 16-byte pieces of the chunk's reverse
-  // state tile (thread t holds row t / 4, columns 16 (t % 4) .. + 15 of each
-  // plane).  Loads are unconditional (rows and chunks clamped to valid memory)
-  // so they stay in flight until the next chunk uses them.
+  // Per-chunk global data: [0] r, [1] k, [2] v, [3] w rows of the lane's home
+  // token, and 2 SP 16-byte pieces of the chunk's reverse-state tile (thread t
+  // holds row t / 4, columns 16 (t % 4) .. + 15 of each plane).  The next
+  // chunk's loads are issued once the current chunk's operands are built and
+  // stay in flight through the contractions.  Rows and chunks are clamped to
+  // valid memory so the loads are unconditional.
   struct Buf {
     Raw<BF16> in[4];
     uint4 sr[BIDIR ? 2 * SP : 1];
@@ -631,7 +674,7 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
     buf.in[2] = gload<BF16>(p.v, off, g);
     buf.in[3] = gload<BF16>(p.w, off, g);
     if constexpr (BIDIR) {
-      const __bf16* src = p.rev + ((int64_t)bh * p.NC + ch) * (SP * PL) + (tid >> 2) * 64 + 16 * (tid & 3);
+      const __bf16* src = p.rev + ((int64_t)bh * p.NC + ch) * (SP * PL) + srow * 64 + scol;
 #pragma unroll
       for (int s = 0; s < SP; ++s) {
         buf.sr[2 * s] = *reinterpret_cast<const uint4*>(src + s * PL);
@@ -639,19 +682,21 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
       }
     }
   };
+  Buf buf;
+  fetch(c0, buf);
 
-  auto body = [&](int ch, Buf& curb, Buf& nxtb) __attribute__((always_inline)) {
-    Raw<BF16>(&cur)[4] = curb.in;
+  for (int ch = c0; ch < c1; ++ch) {
+    Raw<BF16>(&cur)[4] = buf.in;
     const int64_t s0 = (int64_t)ch * LC;
     const int Lv = (int)min<int64_t>(LC, T - s0);
     const bool valid = tau < Lv;
     lds_barrier();
 
-    // ---- phase A: prefetch the next chunk; in-block scan; values; bonus diagonal
-    fetch(min(ch + 1, c1 - 1), nxtb);
+    // ---- phase A: in-block scan; values; bonus diagonal
+    if (Lv < LC) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mask_row<BF16>(cur[i], valid);
-
+      for (int i = 0; i < 4; ++i) mask_row<BF16>(cur[i], valid);
+    }
     float lin[2][8];   // in-block inclusive prefix of lambda
     block_scan<BF16>(cur[3], valid, lin);
     publish_block_totals(lin, sBT, J, g, li);
@@ -674,26 +719,26 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
     lds_barrier();
 
     // ---- phase B: operands
+    float off[2][8], tot[2][8];
     bool slow = false;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      float off[8], tot[8];
-      block_sums(sBT, J, 32 * ks + 8 * g, off, tot);
+      block_sums(sBT, J, 32 * ks + 8 * g, off[ks], tot[ks]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) slow |= tot[j] < -kSpanMax;
+      for (int j = 0; j < 8; ++j) slow |= tot[ks][j] < -kSpanMax;
     }
     slow = __any(slow);   // each wave sees all 64 channels: uniform in the workgroup
     // state entering this chunk from the right: the later chunks of the
-    // segment (prefetched, pre-split) plus, with segments, 2^(rest) R of the
-    // later segments
+    // segment (prefetched, pre-split) plus, with segments, R of the later
+    // segments decayed to this chunk
     const bool right = ch < c1 - 1 || have_R;
     if (BIDIR) {
       if (!RIN || !have_R) {
         if (ch < c1 - 1) {
 #pragma unroll
           for (int s = 0; s < SP; ++s) {
-            *reinterpret_cast<uint4*>(sSr + s * PL + swz(srow, scol)) = curb.sr[2 * s];
-            *reinterpret_cast<uint4*>(sSr + s * PL + swz(srow, scol + 8)) = curb.sr[2 * s + 1];
+            *reinterpret_cast<uint4*>(sSr + s * PL + swz(srow, scol)) = buf.sr[2 * s];
+            *reinterpret_cast<uint4*>(sSr + s * PL + swz(srow, scol + 8)) = buf.sr[2 * s + 1];
           }
         }
       } else {
@@ -705,7 +750,7 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
           for (int s = 0; s < SP; ++s)
 #pragma unroll
             for (int hq = 0; hq < 2; ++hq) {
-              const uint4 q = curb.sr[2 * s + hq];
+              const uint4 q = buf.sr[2 * s + hq];
               const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
@@ -716,81 +761,76 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
         }
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq) {
-          float off[8], tot[8];
-          block_sums(sBT, 0, scol + 8 * hq, off, tot);
+          float o2[8], t2[8];
+          block_sums(sBT, 0, scol + 8 * hq, o2, t2);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            rf[8 * hq + j] -= tot[j];
-            x[8 * hq + j] += ex2(rf[8 * hq + j]) * Rr[8 * hq + j];
+            // fast: the query carries 2^(-Lin), so R enters with the decay from
+            // the chunk start; slow: the query carries 2^(Ltot - Lin)
+            const float before = rf[8 * hq + j];
+            rf[8 * hq + j] -= t2[j];
+            x[8 * hq + j] += ex2(slow ? rf[8 * hq + j] : before) * Rr[8 * hq + j];
           }
         }
         lds_write8<SP>(sSr, srow, scol, x);
         lds_write8<SP>(sSr, srow, scol + 8, x + 8);
       }
     }
-    Op<SP> rq[2], rbq[2];   // queries r 2^Lex and r 2^(Ltot - Lin)
+    Op<SP> rq[2], rbq[2];   // queries r 2^Lex and r 2^(-Lin) (slow: r 2^(Ltot - Lin))
     {
       float r[2][8], k[2][8];
       unpack<BF16>(cur[0], r);
       unpack<BF16>(cur[1], k);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        float off[8], tot[8];
-        block_sums(sBT, J, 32 * ks + 8 * g, off, tot);
         float kf[8], kb[8], qf[8], qb[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int c = 32 * ks + 8 * g + j;
-          const float lin_c = lin[ks][j] + off[j];
-          const float lex_c = row_shr<1>(lin[ks][j]) + off[j];
-          float kt;
+          const float lin_c = lin[ks][j] + off[ks][j];
+          const float lex_c = row_shr<1>(lin[ks][j]) + off[ks][j];
           if (!slow) {
             const float Fc = ex2(-lin_c);
             const float Ec = ex2(lex_c);
             kf[j] = k[ks][j] * Fc;
-            kb[j] = k[ks][j] * Ec * ex2(-tot[j]);
+            kb[j] = k[ks][j] * Ec;
             qf[j] = r[ks][j] * Ec;
-            qb[j] = r[ks][j] * Fc * ex2(tot[j]);
-            kt = kf[j];   // row-scaled by 2^Ltot after the product
+            qb[j] = r[ks][j] * Fc;
           } else {
-            const float eJ = off[j] + sBT[J * 64 + c];
+            const float eJ = off[ks][j] + sBT[J * 64 + c];
             kf[j] = k[ks][j] * ex2(eJ - lin_c);
-            kb[j] = k[ks][j] * ex2(lex_c - off[j]);
+            kb[j] = k[ks][j] * ex2(lex_c - off[ks][j]);
             qf[j] = r[ks][j] * ex2(lex_c);
-            qb[j] = r[ks][j] * ex2(tot[j] - lin_c);
-            kt = k[ks][j] * ex2(tot[j] - lin_c);
+            qb[j] = r[ks][j] * ex2(tot[ks][j] - lin_c);
           }
-          lds_write1<SP>(sKt, c, tau, kt);
-          if (J == 0 && li == 0) sTot[c] = tot[j];
+          if (J == 0 && li == 0) sTot[c] = tot[ks][j];
         }
         lds_write8<SP>(sKf, tau, 32 * ks + 8 * g, kf);
         if (BIDIR) lds_write8<SP>(sKb, tau, 32 * ks + 8 * g, kb);
         rq[ks] = split8<SP>(qf);
-        rbq[ks] = split8<SP>(qb);
+        if (BIDIR) rbq[ks] = split8<SP>(qb);
       }
     }
     lds_barrier();
 
     // ---- phase C: scores, outputs
-    if (16 * J < Lv) {
-      // slow path: the queries of each key block are rebuilt from the current
-      // chunk's r and w, which are still in registers
-      float rs[2][8], lns[2][8], lxs[2][8];
-      if (slow) {
-        float lin2[2][8];
-        block_scan<BF16>(cur[3], valid, lin2);
-        unpack<BF16>(cur[0], rs);
+    // slow path: the queries of each key block are rebuilt from the current
+    // chunk's r and w before the buffers take the next chunk
+    float rs[2][8], lns[2][8], lxs[2][8];
+    if (slow && 16 * J < Lv) {
+      float lin2[2][8];
+      block_scan<BF16>(cur[3], valid, lin2);
+      unpack<BF16>(cur[0], rs);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          float off[8], tot[8];
-          block_sums(sBT, J, 32 * ks + 8 * g, off, tot);
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            lns[ks][j] = lin2[ks][j] + off[j];
-            lxs[ks][j] = row_shr<1>(lin2[ks][j]) + off[j];
-          }
+        for (int j = 0; j < 8; ++j) {
+          lns[ks][j] = lin2[ks][j] + off[ks][j];
+          lxs[ks][j] = row_shr<1>(lin2[ks][j]) + off[ks][j];
         }
-      }
+    }
+    fetch(min(ch + 1, c1 - 1), buf);
+    if (16 * J < Lv) {
       f32x4 M[4];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
@@ -838,7 +878,6 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
           val += (i == tau) ? dg : 0.f;
           M[I][j] = val;
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
 
       f32x4 Y[4];
@@ -860,7 +899,6 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
         for (int nt = 0; nt < 4; ++nt)
           Y[nt] = mma(lds_read4x2<SV>(sV, 16 * nt + li, 16 * I0 + 4 * g, 16 * I1 + 4 * g), mo, Y[nt]);
       }
-      __builtin_amdgcn_sched_barrier(0);
       // Y^T += S^T (r 2^Lex)^T : state from the left
       if (ch > c0 || have_S) {
 #pragma unroll
@@ -869,16 +907,13 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
           for (int nt = 0; nt < 4; ++nt)
             Y[nt] = mma(lds_read8<SP>(sS, 16 * nt + li, 32 * ks + 8 * g), rq[ks], Y[nt]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (BIDIR) {
-        // Y^T += S'^T (r 2^(Ltot - Lin))^T : state from the right
-        if (right) {
+      // Y^T += S'^T (r 2^(-Lin))^T : state from the right (carries 2^Ltot)
+      if (BIDIR && right) {
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              Y[nt] = mma(lds_read8<SP>(sSr, 16 * nt + li, 32 * ks + 8 * g), rbq[ks], Y[nt]);
-        }
+          for (int nt = 0; nt < 4; ++nt)
+            Y[nt] = mma(lds_read8<SP>(sSr, 16 * nt + li, 32 * ks + 8 * g), rbq[ks], Y[nt]);
       }
       if (valid) {
         float* yrow = p.y + base + (s0 + tau) * C;
@@ -888,10 +923,12 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
       }
     }
 
-    if (ch == c1 - 1) return;
+    if (ch == c1 - 1) break;
     lds_barrier();   // every wave has finished reading sS
 
-    // ---- phase D: state rows 16J + 4g + j
+    // ---- phase D: state rows 16J + 4g + j.  Keys k 2^(-Lin) are read down the
+    // columns of sKf; fast: S <- 2^Ltot (S + K^T V); slow: the keys of token
+    // block I are rescaled to k 2^(Ltot - Lin) and S <- 2^Ltot S + K^T V.
     float dec[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) dec[j] = ex2(sTot[16 * J + 4 * g + j]);
@@ -903,7 +940,20 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const Op<SP> key = lds_read8<SP>(sKt, 16 * J + li, 32 * ks + 8 * g);
+      Op<SP> key = lds_read_col8<SP>(sKf, 32 * ks + 8 * g, 16 * J + li);
+      if (slow) {
+        // rows 32ks + 8g .. + 7 lie in token block I = 2ks + g / 2
+        const int c = 16 * J + li;
+        const int I = 2 * ks + (g >> 1);
+        const float eI = block_end(sBT, I, c);
+        const float tc = sTot[c];
+        float x[8];
+        join8<SP>(key, x);
+        const float f = ex2(tc - eI);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] *= f;
+        key = split8<SP>(x);
+      }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         S[nt] = mma(key, lds_read8<SV>(sV, 16 * nt + li, 32 * ks + 8 * g), S[nt]);
@@ -919,13 +969,6 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
       const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
       lds_write4<SP>(sS, 16 * nt + li, 16 * J + 4 * g, x);
     }
-  };
-
-  Buf X, Y;
-  fetch(c0, X);
-  for (int ch = c0; ch < c1; ch += 2) {
-    body(ch, X, Y);
-    if (ch + 1 < c1) body(ch + 1, Y, X);
   }
 }
 
