@@ -112,6 +112,30 @@ def cpu_baseline(w: I.Workload, x: dict, budget_s: float = 20.0) -> dict:
                       f"float64 numpy recurrence, BLAS limited to 1 thread), {el:.1f} s"}
 
 
+def copy_calibration(torch, mib: int, steps: int, warmup: int) -> int:
+    """Copy mib MiB between two device buffers, steps times after warmup
+    copies: a kernel whose HBM bytes are known exactly (mib MiB read and mib
+    MiB written per launch), so rocprofv3's FETCH_SIZE / WRITE_SIZE readings
+    for it give the factor that turns those counters into bytes."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": steps + warmup, "ms_per_copy": ms,
+                      "copy_GBps": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +146,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-rotate", action="store_true",
                     help="reuse one input set (warm Infinity Cache; not the headline number)")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="instead of the operator, time a plain device-to-device copy of MIB "
+                         "MiB (reference kernel for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -129,6 +156,10 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        return copy_calibration(torch, args.copy_calibration, args.steps, args.warmup)
+
     from linear_attention_rnn_amd import wkv6
 
     def device_inputs(xs, dtype):

@@ -88,11 +88,7 @@ constexpr int LC = kChunk;     // chunk length
 constexpr int NT = 256;        // threads per workgroup
 constexpr int PL = HS * LC;    // elements of one 64x64 plane
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kSpanMax = 96.f;   // fast-path bound on the log2 decay of a chunk
-
-#ifndef WKV6_FWD_WAVES
-#define WKV6_FWD_WAVES 1   // waves per SIMD the forward kernel is register-budgeted for
-#endif
+constexpr float kBlockSpan = 24.f;  // fast path: every 16-token block decays by less than 2^-24
 
 struct Params {
   const void* r;
@@ -232,6 +228,98 @@ __device__ __forceinline__ void lds_write1(__bf16* P, int row, int col, float x)
   }
 }
 
+// Lane offsets into the swizzled planes, computed once per kernel so that
+// every plane access is a per-lane base plus an immediate offset.
+//   a[ks]     row li, 16-byte chunk 4 ks + g          (+1024 per 16 rows)
+//   v[pr][h]  row li, 8 bytes at column 16 (2 pr + h) + 4 g
+//   c[j]      row 8 g + j, column tau                  (+2048 per 32 rows)
+//   s         row li, 8 bytes at column 16 J + 4 g
+struct LdsOff {
+  int a[2];
+  int v[2][2];
+  int c[8];
+  int s;
+};
+
+__device__ __forceinline__ LdsOff lds_offsets(int J, int g, int li) {
+  LdsOff o;
+  const int x = li & 7, tau = 16 * J + li;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) o.a[ks] = li * 64 + (((4 * ks + g) ^ x) << 3);
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) o.v[pr][h] = li * 64 + (((4 * pr + 2 * h + (g >> 1)) ^ x) << 3) + 4 * (g & 1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o.c[j] = (8 * g + j) * 64 + ((((tau >> 3)) ^ j) << 3) + (tau & 7);
+  o.s = li * 64 + (((2 * J + (g >> 1)) ^ x) << 3) + 4 * (g & 1);
+  return o;
+}
+
+template <int S>
+__device__ __forceinline__ Op<S> rd8(const __bf16* P, int off) {
+  Op<S> o;
+#pragma unroll
+  for (int s = 0; s < S; ++s) o.p[s] = *reinterpret_cast<const bf16x8*>(P + s * PL + off);
+  return o;
+}
+
+template <int S>
+__device__ __forceinline__ Op<S> rd4x2(const __bf16* P, int o0, int o1) {
+  Op<S> o;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(P + s * PL + o0);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(P + s * PL + o1);
+    o.p[s] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  return o;
+}
+
+// k-slot j from offset add + c[j] (a column read down 8 stored rows)
+template <int S>
+__device__ __forceinline__ Op<S> rdcol8(const __bf16* P, const int (&c)[8], int add) {
+  Op<S> o;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o.p[s][j] = P[s * PL + add + c[j]];
+  return o;
+}
+
+template <int S>
+__device__ __forceinline__ void wr8(__bf16* P, int off, const float* x) {
+  const Op<S> o = split8<S>(x);
+#pragma unroll
+  for (int s = 0; s < S; ++s) *reinterpret_cast<bf16x8*>(P + s * PL + off) = o.p[s];
+}
+
+template <int S>
+__device__ __forceinline__ void wr4(__bf16* P, int off, const float* x) {
+  float r[4] = {x[0], x[1], x[2], x[3]};
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    bf16x4 q;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const __bf16 h = (__bf16)r[j];
+      q[j] = h;
+      r[j] -= (float)h;
+    }
+    *reinterpret_cast<bf16x4*>(P + s * PL + off) = q;
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void wr1(__bf16* P, int off, float x) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const __bf16 h = (__bf16)x;
+    P[s * PL + off] = h;
+    x -= (float)h;
+  }
+}
+
 // ---- split planes in global memory (row-major, unswizzled)
 template <int S>
 __device__ __forceinline__ Op<S> gl_read8(const __bf16* P, int row, int col0) {
@@ -332,10 +420,11 @@ __device__ __forceinline__ void load8f(const float* p, float (&o)[8]) {
 // ---- prefix sums of the chunk for the lane's 16 home elements
 //
 // block_scan: lambda and its inclusive prefix inside the lane's 16-token block
-// (DPP row shifts within each 16-lane row).  block_sums: for 8 consecutive
-// home channels, the sum of the block totals before block J (off) and of all
-// four blocks (tot), read from sBT.  Every consumer sums in the same order, so
-// an exclusive prefix and the preceding inclusive prefix are bit-identical.
+// (DPP row shifts within each 16-lane row; lanes past the sequence end
+// contribute lambda = 0).  Lane 15 of each row then holds the block totals,
+// which go to sBT[J][c].  Block offsets and chunk totals are summed from sBT
+// in block order everywhere, so an exclusive prefix and the preceding
+// inclusive prefix are bit-identical.
 template <bool BF16>
 __device__ __forceinline__ void block_scan(const Raw<BF16>& rw, bool valid, float (&lin)[2][8]) {
   float w[2][8];
@@ -353,7 +442,16 @@ __device__ __forceinline__ void block_scan(const Raw<BF16>& rw, bool valid, floa
     }
 }
 
-__device__ __forceinline__ void publish_block_totals(const float (&lin)[2][8], float* sBT, int J, int g, int li) {
+// Publish the block totals of wave J and whether any channel of the block
+// decays by 2^-kBlockSpan or more (then the chunk takes the slow path).
+__device__ __forceinline__ void publish_block(const float (&lin)[2][8], float* sBT, int* sFlag, int J, int g,
+                                              int li, int lane) {
+  bool big = false;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) big |= lin[ks][j] < -kBlockSpan;
+  big = __any(li == 15 && big);
   if (li == 15) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -362,19 +460,32 @@ __device__ __forceinline__ void publish_block_totals(const float (&lin)[2][8], f
         *reinterpret_cast<float4*>(&sBT[J * 64 + 32 * ks + 8 * g + j]) =
             make_float4(lin[ks][j], lin[ks][j + 1], lin[ks][j + 2], lin[ks][j + 3]);
   }
+  if (lane == 0) sFlag[J] = big ? 1 : 0;
 }
 
-__device__ __forceinline__ void block_sums(const float* sBT, int J, int cb, float (&off)[8], float (&tot)[8]) {
+// A wave whose 16 tokens all lie past the sequence end publishes zero totals.
+__device__ __forceinline__ void publish_empty_block(float* sBT, int* sFlag, int J, int lane) {
+  sBT[J * 64 + lane] = 0.f;
+  if (lane == 0) sFlag[J] = 0;
+}
+
+__device__ __forceinline__ bool chunk_is_slow(const int* sFlag) {
+  const int4 f = *reinterpret_cast<const int4*>(sFlag);
+  return (f.x | f.y | f.z | f.w) != 0;
+}
+
+// Sum of the block totals before block J (the block's offset) for 8
+// consecutive channels.
+__device__ __forceinline__ void block_offset(const float* sBT, int J, int cb, float (&off)[8]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) off[j] = tot[j] = 0.f;
+  for (int j = 0; j < 8; ++j) off[j] = 0.f;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    float b[8];
-    load8f(&sBT[jj * 64 + cb], b);
+  for (int I = 0; I < 3; ++I) {
+    if (I < J) {
+      float b[8];
+      load8f(&sBT[I * 64 + cb], b);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (jj < J) off[j] += b[j];
-      tot[j] += b[j];
+      for (int j = 0; j < 8; ++j) off[j] += b[j];
     }
   }
 }
@@ -394,14 +505,88 @@ __device__ __forceinline__ void block_end8(const float* sBT, int I, int cb, floa
   }
 }
 
-// Prefix at the end of token block I (E_I) for one channel, summed in the
-// order block_sums uses.
+// Chunk totals (Ltot) of 4 consecutive channels.
+__device__ __forceinline__ void chunk_total4(const float* sBT, int cb, float (&t)[4]) {
+  float4 a = *reinterpret_cast<const float4*>(&sBT[cb]);
+  t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w;
+#pragma unroll
+  for (int I = 1; I < 4; ++I) {
+    a = *reinterpret_cast<const float4*>(&sBT[I * 64 + cb]);
+    t[0] += a.x; t[1] += a.y; t[2] += a.z; t[3] += a.w;
+  }
+}
+
+// Prefix at the end of token block I (E_I) for one channel.
 __device__ __forceinline__ float block_end(const float* sBT, int I, int c) {
   float o = 0.f;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj)
     if (jj <= I) o += sBT[jj * 64 + c];
   return o;
+}
+
+// ---- LDS clears for token blocks past the sequence end
+// planes stored [row][t]: columns t0 .. t0 + 15 of all 64 rows
+template <int S>
+__device__ __forceinline__ void zero_cols16(__bf16* P, int t0, int lane) {
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq)
+      *reinterpret_cast<uint4*>(P + s * PL + swz(lane, t0 + 8 * hq)) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// planes stored [t][col]: rows t0 .. t0 + 15, all 64 columns
+template <int S>
+__device__ __forceinline__ void zero_rows16(__bf16* P, int t0, int lane) {
+  const int row = t0 + (lane >> 2), cb = 16 * (lane & 3);
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq)
+      *reinterpret_cast<uint4*>(P + s * PL + swz(row, cb + 8 * hq)) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Column read of a split plane set: k-slots j = 0..7 are rows r0 + j of
+// column col (an A operand whose K dimension runs down the stored rows).
+template <int S>
+__device__ __forceinline__ Op<S> lds_read_col8(const __bf16* P, int r0, int col) {
+  Op<S> o;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o.p[s][j] = P[s * PL + swz(r0 + j, col)];
+  return o;
+}
+
+template <int S>
+__device__ __forceinline__ void join8(const Op<S>& o, float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v = 0.f;
+#pragma unroll
+    for (int s = S - 1; s >= 0; --s) v += (float)o.p[s][j];
+    x[j] = v;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack_half(const Raw<BF16>& r, int ks, float (&o)[8]) {
+  if constexpr (BF16) {
+    const uint4 q = r.q[ks];
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = __uint_as_float(w4[j] << 16);
+      o[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
+    }
+  } else {
+    const uint4 a = r.q[2 * ks], b = r.q[2 * ks + 1];
+    o[0] = __uint_as_float(a.x); o[1] = __uint_as_float(a.y);
+    o[2] = __uint_as_float(a.z); o[3] = __uint_as_float(a.w);
+    o[4] = __uint_as_float(b.x); o[5] = __uint_as_float(b.y);
+    o[6] = __uint_as_float(b.z); o[7] = __uint_as_float(b.w);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -411,19 +596,21 @@ __device__ __forceinline__ float block_end(const float* sBT, int I, int c) {
 // own total decay 2^Ltot when the chunk takes the fast path (the forward
 // kernel then pairs it with the query r 2^(-Lin)), unscaled otherwise.
 template <bool BF16, bool BIDIR, bool CARRY>
-__global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
+__global__ __launch_bounds__(NT, BF16 ? 2 : 1) void seg_kernel(Params p) {
   constexpr int SP = BF16 ? 2 : 3;
   constexpr int SV = BF16 ? 1 : 3;
   __shared__ __attribute__((aligned(16))) __bf16 sEb[BIDIR ? SP * PL : 8];   // (k 2^Lex)^T   [c][t]
   __shared__ __attribute__((aligned(16))) __bf16 sEf[CARRY ? SP * PL : 8];   // (k 2^(Ltot-Lin+D))^T
   __shared__ __attribute__((aligned(16))) __bf16 sV[SV * PL];                 // V^T [n][t]
   __shared__ __attribute__((aligned(16))) float sBT[4 * 64];
-  __shared__ __attribute__((aligned(16))) float sTot[64];
+  __shared__ __attribute__((aligned(16))) int sFlag[4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, J = tid >> 6;
+  const int lane = tid & 63;
+  const int J = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
   const int tau = 16 * J + li;
+  const LdsOff lo = lds_offsets(J, g, li);
   const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
   const int b = bh / p.H, h = bh % p.H;
   const int64_t T = p.T, C = p.C;
@@ -451,54 +638,78 @@ __global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
   };
 
   auto body = [&](int ch, Raw<BF16> (&cur)[3], Raw<BF16> (&nxt)[3]) __attribute__((always_inline)) {
-    const bool valid = (int64_t)ch * LC + tau < T;
+    const int Lv = (int)min<int64_t>(LC, T - (int64_t)ch * LC);
+    const bool valid = tau < Lv;
+    const bool active = 16 * J < Lv;   // uniform in the wave
     lds_barrier();
     fetch(max(ch - 1, c0), nxt);
-    if ((int64_t)ch * LC + LC > T) {
-#pragma unroll
-      for (int i = 0; i < 3; ++i) mask_row<BF16>(cur[i], valid);
-    }
+
+    // ---- phase A: scan, block totals, values
     float lin[2][8];
-    block_scan<BF16>(cur[2], valid, lin);
-    publish_block_totals(lin, sBT, J, g, li);
-    {
-      float v[2][8];
-      unpack<BF16>(cur[1], v);
+    if (active) {
+      if (Lv < LC) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) lds_write1<SV>(sV, 32 * ks + 8 * g + j, tau, v[ks][j]);
-    }
-    lds_barrier();
-    bool slow = false;
-    {
-      float k[2][8];
-      unpack<BF16>(cur[0], k);
+        for (int i = 0; i < 3; ++i) mask_row<BF16>(cur[i], valid);
+      }
+      block_scan<BF16>(cur[2], valid, lin);
+      publish_block(lin, sBT, sFlag, J, g, li, lane);
+      float v[8];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        float off[8], tot[8];
-        block_sums(sBT, J, 32 * ks + 8 * g, off, tot);
+        unpack_half<BF16>(cur[1], ks, v);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = 32 * ks + 8 * g + j;
-          slow |= tot[j] < -kSpanMax;
-          const float lin_c = lin[ks][j] + off[j];
-          const float lex_c = row_shr<1>(lin[ks][j]) + off[j];
-          if (BIDIR) lds_write1<SP>(sEb, c, tau, k[ks][j] * ex2(lex_c));
-          if (CARRY) {
-            lds_write1<SP>(sEf, c, tau, k[ks][j] * ex2(tot[j] - lin_c + D[ks][j]));
-            D[ks][j] += tot[j];
-          }
-          if (J == 0 && li == 0) sTot[c] = tot[j];
-        }
+        for (int j = 0; j < 8; ++j) wr1<SV>(sV, 2048 * ks + lo.c[j], v[j]);
       }
+    } else {
+      publish_empty_block(sBT, sFlag, J, lane);
+      zero_cols16<SV>(sV, 16 * J, lane);
+      if (BIDIR) zero_cols16<SP>(sEb, 16 * J, lane);
+      if (CARRY) zero_cols16<SP>(sEf, 16 * J, lane);
     }
-    slow = __any(slow);   // every wave sees all 64 channels: uniform in the workgroup
     lds_barrier();
 
-    float dec[4];
+    // ---- phase B: decayed keys, stored transposed
+    const bool slow = chunk_is_slow(sFlag);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dec[j] = ex2(sTot[16 * J + 4 * g + j]);
+    for (int ks = 0; ks < 2; ++ks) {
+      const int cb = 32 * ks + 8 * g;
+      float tot[8];
+      if (CARRY) {
+        float4 t0, t1;
+        t0 = *reinterpret_cast<const float4*>(&sBT[cb]);
+        t1 = *reinterpret_cast<const float4*>(&sBT[cb + 4]);
+        tot[0] = t0.x; tot[1] = t0.y; tot[2] = t0.z; tot[3] = t0.w;
+        tot[4] = t1.x; tot[5] = t1.y; tot[6] = t1.z; tot[7] = t1.w;
+#pragma unroll
+        for (int I = 1; I < 4; ++I) {
+          float bb[8];
+          load8f(&sBT[I * 64 + cb], bb);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) tot[j] += bb[j];
+        }
+      }
+      if (active) {
+        float off[8], k[8];
+        block_offset(sBT, J, cb, off);
+        unpack_half<BF16>(cur[0], ks, k);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (BIDIR) wr1<SP>(sEb, 2048 * ks + lo.c[j], k[j] * ex2(row_shr<1>(lin[ks][j]) + off[j]));
+          if (CARRY) wr1<SP>(sEf, 2048 * ks + lo.c[j], k[j] * ex2(tot[j] - (lin[ks][j] + off[j]) + D[ks][j]));
+        }
+      }
+      if (CARRY) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) D[ks][j] += tot[j];
+      }
+    }
+    lds_barrier();
+
+    // ---- phase D: state rows 16J + 4g + j
+    float tot4[4], dec[4];
+    chunk_total4(sBT, 16 * J + 4 * g, tot4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dec[j] = ex2(tot4[j]);
     // state each chunk receives from the later chunks of the segment
     if (BIDIR && ch < c1 - 1) {
       __bf16* dst = p.rev + ((int64_t)bh * p.NC + ch) * (SP * PL);
@@ -519,12 +730,13 @@ __global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      if (32 * ks >= Lv) break;
       Op<SP> eb, ef;
-      if (BIDIR) eb = lds_read8<SP>(sEb, 16 * J + li, 32 * ks + 8 * g);
-      if (CARRY) ef = lds_read8<SP>(sEf, 16 * J + li, 32 * ks + 8 * g);
+      if (BIDIR) eb = rd8<SP>(sEb, 1024 * J + lo.a[ks]);
+      if (CARRY) ef = rd8<SP>(sEf, 1024 * J + lo.a[ks]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const Op<SV> vb = lds_read8<SV>(sV, 16 * nt + li, 32 * ks + 8 * g);
+        const Op<SV> vb = rd8<SV>(sV, 1024 * nt + lo.a[ks]);
         if (BIDIR) Sb[nt] = mma(eb, vb, Sb[nt]);
         if (CARRY) F[nt] = mma(ef, vb, F[nt]);
       }
@@ -556,33 +768,10 @@ __global__ __launch_bounds__(NT, 2) void seg_kernel(Params p) {
   }
 }
 
-// Column read of a split plane set: k-slots j = 0..7 are rows r0 + j of
-// column col (an A operand whose K dimension runs down the stored rows).
-template <int S>
-__device__ __forceinline__ Op<S> lds_read_col8(const __bf16* P, int r0, int col) {
-  Op<S> o;
-#pragma unroll
-  for (int s = 0; s < S; ++s)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o.p[s][j] = P[s * PL + swz(r0 + j, col)];
-  return o;
-}
-
-template <int S>
-__device__ __forceinline__ void join8(const Op<S>& o, float (&x)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float v = 0.f;
-#pragma unroll
-    for (int s = S - 1; s >= 0; --s) v += (float)o.p[s][j];
-    x[j] = v;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Main sweep: outputs of one segment, left to right.
 template <bool BF16, bool BIDIR, bool CARRY>
-__global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
+__global__ __launch_bounds__(NT, BF16 ? 2 : 1) void fwd_kernel(Params p) {
   constexpr int SP = BF16 ? 2 : 3;
   constexpr int SV = BF16 ? 1 : 3;
   constexpr bool RIN = BIDIR && CARRY;
@@ -592,13 +781,15 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) __bf16 sS[SP * PL];               // S^T [n][c]
   __shared__ __attribute__((aligned(16))) __bf16 sSr[BIDIR ? SP * PL : 8];  // S'^T [n][c] entering this chunk
   __shared__ __attribute__((aligned(16))) float sBT[4 * 64];
-  __shared__ __attribute__((aligned(16))) float sTot[64];
   __shared__ __attribute__((aligned(16))) float sU[64];
+  __shared__ __attribute__((aligned(16))) int sFlag[4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, J = tid >> 6;
+  const int lane = tid & 63;
+  const int J = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
   const int tau = 16 * J + li;   // home token of the lane (also its output column)
+  const LdsOff lo = lds_offsets(J, g, li);
   const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
   const int b = bh / p.H, h = bh % p.H;
   const int64_t T = p.T, C = p.C;
@@ -615,9 +806,9 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
   // State from the later segments, for the staging elements of this thread
   // (row tid / 4, columns 16 (tid % 4) .. + 15 of S'^T), and the log2 decay
   // from the current chunk's start to the end of this segment for those columns.
-  float Rr[16], rf[16];
+  float Rr[RIN ? 16 : 1], rf[RIN ? 16 : 1];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) Rr[j] = rf[j] = 0.f;
+  for (int j = 0; j < (RIN ? 16 : 1); ++j) Rr[j] = rf[j] = 0.f;
   const int srow = tid >> 2, scol = 16 * (tid & 3);
   bool have_S = false, have_R = false;
   if (CARRY) {
@@ -637,7 +828,7 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
-        lds_write4<SP>(sS, 16 * nt + li, 16 * J + 4 * g, x);
+        wr4<SP>(sS, 1024 * nt + lo.s, x);
       }
     }
     if (RIN) {
@@ -647,11 +838,11 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
           const float* Rs = sm + (int64_t)s2 * kSummFloats + PL;
           const float* gs = sm + (int64_t)s2 * kSummFloats + 2 * PL;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) Rr[j] = Rr[j] * ex2(gs[scol + j]) + Rs[srow * HS + scol + j];
+          for (int j = 0; j < (RIN ? 16 : 1); ++j) Rr[j] = Rr[j] * ex2(gs[scol + j]) + Rs[srow * HS + scol + j];
         }
         const float* gseg = sm + (int64_t)seg * kSummFloats + 2 * PL;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) rf[j] = gseg[scol + j];
+        for (int j = 0; j < (RIN ? 16 : 1); ++j) rf[j] = gseg[scol + j];
       }
     }
   }
@@ -686,52 +877,42 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
   fetch(c0, buf);
 
   for (int ch = c0; ch < c1; ++ch) {
-    Raw<BF16>(&cur)[4] = buf.in;
     const int64_t s0 = (int64_t)ch * LC;
     const int Lv = (int)min<int64_t>(LC, T - s0);
     const bool valid = tau < Lv;
+    const bool active = 16 * J < Lv;   // uniform in the wave
+    const bool left = ch > c0 || have_S;
+    const bool right = BIDIR && (ch < c1 - 1 || have_R);
     lds_barrier();
 
-    // ---- phase A: in-block scan; values; bonus diagonal
-    if (Lv < LC) {
+    // ---- phase A: in-block scan, block totals, values
+    float lin[2][8];
+    if (active) {
+      if (Lv < LC) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mask_row<BF16>(cur[i], valid);
+        for (int i = 0; i < 4; ++i) mask_row<BF16>(buf.in[i], valid);
+      }
+      block_scan<BF16>(buf.in[3], valid, lin);
+      publish_block(lin, sBT, sFlag, J, g, li, lane);
+      float v[8];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        unpack_half<BF16>(buf.in[2], ks, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wr1<SV>(sV, 2048 * ks + lo.c[j], v[j]);
+      }
+    } else {
+      publish_empty_block(sBT, sFlag, J, lane);
+      zero_cols16<SV>(sV, 16 * J, lane);
+      zero_rows16<SP>(sKf, 16 * J, lane);
+      if (BIDIR) zero_rows16<SP>(sKb, 16 * J, lane);
     }
-    float lin[2][8];   // in-block inclusive prefix of lambda
-    block_scan<BF16>(cur[3], valid, lin);
-    publish_block_totals(lin, sBT, J, g, li);
-    float dg = 0.f;
-    {
-      float r[2][8], k[2][8], v[2][8];
-      unpack<BF16>(cur[0], r);
-      unpack<BF16>(cur[1], k);
-      unpack<BF16>(cur[2], v);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          dg += r[ks][j] * sU[32 * ks + 8 * g + j] * k[ks][j];
-          lds_write1<SV>(sV, 32 * ks + 8 * g + j, tau, v[ks][j]);
-        }
-    }
-    dg += __shfl_xor(dg, 16);
-    dg += __shfl_xor(dg, 32);
     lds_barrier();
 
-    // ---- phase B: operands
-    float off[2][8], tot[2][8];
-    bool slow = false;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      block_sums(sBT, J, 32 * ks + 8 * g, off[ks], tot[ks]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) slow |= tot[ks][j] < -kSpanMax;
-    }
-    slow = __any(slow);   // each wave sees all 64 channels: uniform in the workgroup
-    // state entering this chunk from the right: the later chunks of the
-    // segment (prefetched, pre-split) plus, with segments, R of the later
-    // segments decayed to this chunk
-    const bool right = ch < c1 - 1 || have_R;
+    const bool slow = chunk_is_slow(sFlag);
+    // ---- phase B0: state entering this chunk from the right: the later
+    // chunks of the segment (prefetched, pre-split) plus, with segments, R of
+    // the later segments decayed to this chunk
     if (BIDIR) {
       if (!RIN || !have_R) {
         if (ch < c1 - 1) {
@@ -760,167 +941,259 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
             }
         }
 #pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
-          float o2[8], t2[8];
-          block_sums(sBT, 0, scol + 8 * hq, o2, t2);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float t2[4];
+          chunk_total4(sBT, scol + 4 * q4, t2);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
+          for (int j = 0; j < 4; ++j) {
+            const int jj = 4 * q4 + j;
             // fast: the query carries 2^(-Lin), so R enters with the decay from
             // the chunk start; slow: the query carries 2^(Ltot - Lin)
-            const float before = rf[8 * hq + j];
-            rf[8 * hq + j] -= t2[j];
-            x[8 * hq + j] += ex2(slow ? rf[8 * hq + j] : before) * Rr[8 * hq + j];
+            const float before = rf[jj];
+            rf[jj] -= t2[j];
+            x[jj] += ex2(slow ? rf[jj] : before) * Rr[jj];
           }
         }
         lds_write8<SP>(sSr, srow, scol, x);
         lds_write8<SP>(sSr, srow, scol + 8, x + 8);
       }
     }
-    Op<SP> rq[2], rbq[2];   // queries r 2^Lex and r 2^(-Lin) (slow: r 2^(Ltot - Lin))
-    {
-      float r[2][8], k[2][8];
-      unpack<BF16>(cur[0], r);
-      unpack<BF16>(cur[1], k);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        float kf[8], kb[8], qf[8], qb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = 32 * ks + 8 * g + j;
-          const float lin_c = lin[ks][j] + off[ks][j];
-          const float lex_c = row_shr<1>(lin[ks][j]) + off[ks][j];
-          if (!slow) {
-            const float Fc = ex2(-lin_c);
-            const float Ec = ex2(lex_c);
-            kf[j] = k[ks][j] * Fc;
-            kb[j] = k[ks][j] * Ec;
-            qf[j] = r[ks][j] * Ec;
-            qb[j] = r[ks][j] * Fc;
-          } else {
-            const float eJ = off[ks][j] + sBT[J * 64 + c];
-            kf[j] = k[ks][j] * ex2(eJ - lin_c);
-            kb[j] = k[ks][j] * ex2(lex_c - off[ks][j]);
-            qf[j] = r[ks][j] * ex2(lex_c);
-            qb[j] = r[ks][j] * ex2(tot[ks][j] - lin_c);
-          }
-          if (J == 0 && li == 0) sTot[c] = tot[ks][j];
-        }
-        lds_write8<SP>(sKf, tau, 32 * ks + 8 * g, kf);
-        if (BIDIR) lds_write8<SP>(sKb, tau, 32 * ks + 8 * g, kb);
-        rq[ks] = split8<SP>(qf);
-        if (BIDIR) rbq[ks] = split8<SP>(qb);
-      }
-    }
-    lds_barrier();
 
-    // ---- phase C: scores, outputs
-    // slow path: the queries of each key block are rebuilt from the current
-    // chunk's r and w before the buffers take the next chunk
-    float rs[2][8], lns[2][8], lxs[2][8];
-    if (slow && 16 * J < Lv) {
-      float lin2[2][8];
-      block_scan<BF16>(cur[3], valid, lin2);
-      unpack<BF16>(cur[0], rs);
+    if (!slow) {
+      // ---- phase B (fast): keys k 2^(-Lin) (past) and k 2^Lex (later) to LDS;
+      // queries r 2^Lex and r 2^(-Lin) kept split in registers; bonus diagonal
+      Op<SP> rq[2], rbq[2];
+      float dg = 0.f;
+      if (active) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
+          const int cb = 32 * ks + 8 * g;
+          float off[8], r[8], k[8], uu[8];
+          block_offset(sBT, J, cb, off);
+          unpack_half<BF16>(buf.in[0], ks, r);
+          unpack_half<BF16>(buf.in[1], ks, k);
+          load8f(&sU[cb], uu);
+          float kf[8], kb[8], qf[8], qb[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          lns[ks][j] = lin2[ks][j] + off[ks][j];
-          lxs[ks][j] = row_shr<1>(lin2[ks][j]) + off[ks][j];
-        }
-    }
-    fetch(min(ch + 1, c1 - 1), buf);
-    if (16 * J < Lv) {
-      f32x4 M[4];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-        if (I <= J) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const Op<SP> key = lds_read8<SP>(sKf, 16 * I + li, 32 * ks + 8 * g);
-            if (!slow) {
-              a = mma(key, rq[ks], a);
-            } else {
-              float e[8], q[8];
-              block_end8(sBT, I, 32 * ks + 8 * g, e);
-#pragma unroll
-              for (int j = 0; j < 8; ++j) q[j] = rs[ks][j] * ex2(lxs[ks][j] - e[j]);
-              a = mma(key, split8<SP>(q), a);
-            }
+          for (int j = 0; j < 8; ++j) {
+            const float Fc = ex2(-(lin[ks][j] + off[j]));
+            const float Ec = ex2(row_shr<1>(lin[ks][j]) + off[j]);
+            kf[j] = k[j] * Fc;
+            kb[j] = k[j] * Ec;
+            qf[j] = r[j] * Ec;
+            qb[j] = r[j] * Fc;
+            dg += r[j] * uu[j] * k[j];
           }
+          wr8<SP>(sKf, 1024 * J + lo.a[ks], kf);
+          if (BIDIR) wr8<SP>(sKb, 1024 * J + lo.a[ks], kb);
+          rq[ks] = split8<SP>(qf);
+          if (BIDIR) rbq[ks] = split8<SP>(qb);
         }
-        if (BIDIR && I >= J) {
+        dg += __shfl_xor(dg, 16);
+        dg += __shfl_xor(dg, 32);
+      }
+      fetch(min(ch + 1, c1 - 1), buf);
+      lds_barrier();
+
+      // ---- phase C (fast): scores, outputs
+      if (active) {
+        f32x4 Y[4];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const Op<SP> key = lds_read8<SP>(sKb, 16 * I + li, 32 * ks + 8 * g);
-            if (!slow) {
-              a2 = mma(key, rbq[ks], a2);
-            } else {
-              float e[8], q[8];
-              if (I) {
-                block_end8(sBT, I - 1, 32 * ks + 8 * g, e);
-              } else {
+        for (int nt = 0; nt < 4; ++nt) Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 8; ++j) e[j] = 0.f;
+        for (int pr = 0; pr < 2; ++pr) {
+          const int I0 = 2 * pr;
+          if ((!BIDIR && I0 > J) || 16 * I0 >= Lv) break;
+          float mx[8];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int I = I0 + hh;
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+            if (16 * I < Lv) {
+              if (I <= J) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) a = mma(rd8<SP>(sKf, 1024 * I + lo.a[ks]), rq[ks], a);
               }
+              if (BIDIR && I >= J) {
 #pragma unroll
-              for (int j = 0; j < 8; ++j) q[j] = rs[ks][j] * ex2(e[j] - lns[ks][j]);
-              a2 = mma(key, split8<SP>(q), a2);
+                for (int ks = 0; ks < 2; ++ks) a2 = mma(rd8<SP>(sKb, 1024 * I + lo.a[ks]), rbq[ks], a2);
+              }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 16 * I + 4 * g + j;
+              float val;
+              if (I < J) val = a[j];
+              else if (I > J) val = a2[j];
+              else val = i < tau ? a[j] : (i > tau ? a2[j] : dg);
+              mx[4 * hh + j] = val;
             }
           }
-        }
+          const Op<SP> mo = split8<SP>(mx);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 16 * I + 4 * g + j;
-          float val = (i < tau) ? a[j] : 0.f;
-          if (BIDIR) val += (i > tau) ? a2[j] : 0.f;
-          val += (i == tau) ? dg : 0.f;
-          M[I][j] = val;
+          for (int nt = 0; nt < 4; ++nt)
+            Y[nt] = mma(rd4x2<SV>(sV, 1024 * nt + lo.v[pr][0], 1024 * nt + lo.v[pr][1]), mo, Y[nt]);
+        }
+        // Y^T += S^T (r 2^Lex)^T : state from the left
+        if (left) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+              Y[nt] = mma(rd8<SP>(sS, 1024 * nt + lo.a[ks]), rq[ks], Y[nt]);
+        }
+        // Y^T += S'^T (r 2^(-Lin))^T : state from the right (carries 2^Ltot)
+        if (right) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+              Y[nt] = mma(rd8<SP>(sSr, 1024 * nt + lo.a[ks]), rbq[ks], Y[nt]);
+        }
+        if (valid) {
+          float* yrow = p.y + base + (s0 + tau) * C;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            *reinterpret_cast<float4*>(yrow + 16 * nt + 4 * g) = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
         }
       }
+    } else {
+      // ---- phase B (slow): each key block I uses references at its own
+      // boundaries: past keys k 2^(E_J - Lin) with queries r 2^(Lex - E_I),
+      // later keys k 2^(Lex - B_J) with queries r 2^(B_I - Lin).  The state
+      // products use r 2^Lex and r 2^(Ltot - Lin).  All queries are built in
+      // phase C from the raw r and w words, so the next chunk's loads wait
+      // until phase C is done.
+      float dg = 0.f;
+      if (active) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int cb = 32 * ks + 8 * g;
+          float off[8], r[8], k[8], uu[8];
+          block_offset(sBT, J, cb, off);
+          unpack_half<BF16>(buf.in[0], ks, r);
+          unpack_half<BF16>(buf.in[1], ks, k);
+          load8f(&sU[cb], uu);
+          float kf[8], kb[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int c = cb + j;
+            const float lin_c = lin[ks][j] + off[j];
+            const float lex_c = row_shr<1>(lin[ks][j]) + off[j];
+            const float eJ = off[j] + sBT[J * 64 + c];
+            kf[j] = k[j] * ex2(eJ - lin_c);
+            kb[j] = k[j] * ex2(lex_c - off[j]);
+            dg += r[j] * uu[j] * k[j];
+          }
+          wr8<SP>(sKf, 1024 * J + lo.a[ks], kf);
+          if (BIDIR) wr8<SP>(sKb, 1024 * J + lo.a[ks], kb);
+        }
+        dg += __shfl_xor(dg, 16);
+        dg += __shfl_xor(dg, 32);
+      }
+      lds_barrier();
 
-      f32x4 Y[4];
+      // ---- phase C (slow)
+      if (active) {
+        // Lin and Lex of the lane's elements, rebuilt from the raw w words
+        float lns[2][8], lxs[2][8];
+        block_scan<BF16>(buf.in[3], valid, lns);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // Y^T[n][tau] += V^T[n][i] M^T[i][tau]
+        for (int ks = 0; ks < 2; ++ks) {
+          float off[8];
+          block_offset(sBT, J, 32 * ks + 8 * g, off);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int I0 = 2 * ks, I1 = 2 * ks + 1;
-        if (!BIDIR && I0 > J) continue;
-        float mx[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          mx[j] = M[I0][j];
-          mx[4 + j] = M[I1][j];
+          for (int j = 0; j < 8; ++j) {
+            lxs[ks][j] = row_shr<1>(lns[ks][j]) + off[j];
+            lns[ks][j] += off[j];
+          }
         }
-        const Op<SP> mo = split8<SP>(mx);
+        f32x4 Y[4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          Y[nt] = mma(lds_read4x2<SV>(sV, 16 * nt + li, 16 * I0 + 4 * g, 16 * I1 + 4 * g), mo, Y[nt]);
-      }
-      // Y^T += S^T (r 2^Lex)^T : state from the left
-      if (ch > c0 || have_S) {
+        for (int nt = 0; nt < 4; ++nt) Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // state products: S^T (r 2^Lex)^T and S'^T (r 2^(Ltot - Lin))^T
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
+          float r[8], q[8];
+          unpack_half<BF16>(buf.in[0], ks, r);
+          if (left) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = r[j] * ex2(lxs[ks][j]);
+            const Op<SP> qo = split8<SP>(q);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) Y[nt] = mma(rd8<SP>(sS, 1024 * nt + lo.a[ks]), qo, Y[nt]);
+          }
+          if (right) {
+            float tot[8];
+            block_end8(sBT, 3, 32 * ks + 8 * g, tot);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = r[j] * ex2(tot[j] - lns[ks][j]);
+            const Op<SP> qo = split8<SP>(q);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) Y[nt] = mma(rd8<SP>(sSr, 1024 * nt + lo.a[ks]), qo, Y[nt]);
+          }
+        }
+        // score tiles, key block by key block
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const int I0 = 2 * pr;
+          if ((!BIDIR && I0 > J) || 16 * I0 >= Lv) break;
+          float mx[8];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int I = I0 + hh;
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+            if (16 * I < Lv) {
+              if (I <= J) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                  float e[8], r[8], q[8];
+                  block_end8(sBT, I, 32 * ks + 8 * g, e);
+                  unpack_half<BF16>(buf.in[0], ks, r);
+#pragma unroll
+                  for (int j = 0; j < 8; ++j) q[j] = r[j] * ex2(lxs[ks][j] - e[j]);
+                  a = mma(rd8<SP>(sKf, 1024 * I + lo.a[ks]), split8<SP>(q), a);
+                }
+              }
+              if (BIDIR && I >= J) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                  float e[8], r[8], q[8];
+                  if (I) {
+                    block_end8(sBT, I - 1, 32 * ks + 8 * g, e);
+                  } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) e[j] = 0.f;
+                  }
+                  unpack_half<BF16>(buf.in[0], ks, r);
+#pragma unroll
+                  for (int j = 0; j < 8; ++j) q[j] = r[j] * ex2(e[j] - lns[ks][j]);
+                  a2 = mma(rd8<SP>(sKb, 1024 * I + lo.a[ks]), split8<SP>(q), a2);
+                }
+              }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 16 * I + 4 * g + j;
+              float val = (i < tau) ? a[j] : 0.f;
+              if (BIDIR) val += (i > tau) ? a2[j] : 0.f;
+              val += (i == tau) ? dg : 0.f;
+              mx[4 * hh + j] = val;
+            }
+          }
+          const Op<SP> mo = split8<SP>(mx);
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt)
-            Y[nt] = mma(lds_read8<SP>(sS, 16 * nt + li, 32 * ks + 8 * g), rq[ks], Y[nt]);
-      }
-      // Y^T += S'^T (r 2^(-Lin))^T : state from the right (carries 2^Ltot)
-      if (BIDIR && right) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            Y[nt] = mma(rd4x2<SV>(sV, 1024 * nt + lo.v[pr][0], 1024 * nt + lo.v[pr][1]), mo, Y[nt]);
+        }
+        if (valid) {
+          float* yrow = p.y + base + (s0 + tau) * C;
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt)
-            Y[nt] = mma(lds_read8<SP>(sSr, 16 * nt + li, 32 * ks + 8 * g), rbq[ks], Y[nt]);
+            *reinterpret_cast<float4*>(yrow + 16 * nt + 4 * g) = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
+        }
       }
-      if (valid) {
-        float* yrow = p.y + base + (s0 + tau) * C;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          *reinterpret_cast<float4*>(yrow + 16 * nt + 4 * g) = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
-      }
+      fetch(min(ch + 1, c1 - 1), buf);
     }
 
     if (ch == c1 - 1) break;
@@ -929,45 +1202,50 @@ __global__ __launch_bounds__(NT, WKV6_FWD_WAVES) void fwd_kernel(Params p) {
     // ---- phase D: state rows 16J + 4g + j.  Keys k 2^(-Lin) are read down the
     // columns of sKf; fast: S <- 2^Ltot (S + K^T V); slow: the keys of token
     // block I are rescaled to k 2^(Ltot - Lin) and S <- 2^Ltot S + K^T V.
-    float dec[4];
+    float tot4[4], dec[4];
+    chunk_total4(sBT, 16 * J + 4 * g, tot4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dec[j] = ex2(sTot[16 * J + 4 * g + j]);
-    if (slow) {
+    for (int j = 0; j < 4; ++j) dec[j] = ex2(tot4[j]);
+    if (!slow) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const Op<SP> key = rdcol8<SP>(sKf, lo.c, 2048 * ks);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          S[nt] = mma(key, rd8<SV>(sV, 1024 * nt + lo.a[ks]), S[nt]);
+      }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) S[nt][j] *= dec[j];
-    }
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      Op<SP> key = lds_read_col8<SP>(sKf, 32 * ks + 8 * g, 16 * J + li);
-      if (slow) {
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[nt][j] *= dec[j];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Op<SP> key = rdcol8<SP>(sKf, lo.c, 2048 * ks);
         // rows 32ks + 8g .. + 7 lie in token block I = 2ks + g / 2
         const int c = 16 * J + li;
         const int I = 2 * ks + (g >> 1);
         const float eI = block_end(sBT, I, c);
-        const float tc = sTot[c];
+        const float tc = block_end(sBT, 3, c);
         float x[8];
         join8<SP>(key, x);
         const float f = ex2(tc - eI);
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] *= f;
         key = split8<SP>(x);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          S[nt] = mma(key, rd8<SV>(sV, 1024 * nt + lo.a[ks]), S[nt]);
       }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        S[nt] = mma(key, lds_read8<SV>(sV, 16 * nt + li, 32 * ks + 8 * g), S[nt]);
-    }
-    if (!slow) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[nt][j] *= dec[j];
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
-      lds_write4<SP>(sS, 16 * nt + li, 16 * J + 4 * g, x);
+      wr4<SP>(sS, 1024 * nt + lo.s, x);
     }
   }
 }
@@ -983,8 +1261,10 @@ Plan plan(const FwdArgs& a) {
   int G = 1;
   if (const char* e = getenv("WKV6_SEGMENTS")) {
     G = atoi(e);
-  } else if (bh < 256) {
-    G = (int)((256 + bh - 1) / bh);
+  } else {
+    // enough workgroups for every CU: two resident per CU for bf16 inputs
+    const int64_t target = a.bf16 ? 512 : 256;
+    if (bh < target) G = (int)((target + bh - 1) / bh);
   }
   G = max(1, min(G, pl.NC));
   pl.CPS = (pl.NC + G - 1) / G;
