@@ -97,17 +97,30 @@ struct Params {
   const void* w;
   const float* u;
   float* y;
-  __bf16* rev;   // [B*H][NC][SP planes][64 n][64 c]: state from the later chunks of the segment
-  float* summ;   // [B*H][G]{F^T[64][64], R^T[64][64], g[64]} when G > 1
+  float* summ;   // [B*H][G][direction]{S^T[64][64], g[64]} when G > 1
   int64_t T;
   int64_t C;
   int H;
-  int NC;   // chunks per sequence
-  int CPS;  // chunks per segment
-  int G;    // segments per sequence
+  int G;      // segments per sequence
+  int SEGC;   // chunks per segment (the last segment may be shorter)
 };
 
-constexpr int kSummFloats = 2 * PL + HS;
+constexpr int kSummFloats = PL + HS;
+
+enum SweepMode { kState = 0, kOut = 1, kOutAcc = 2 };
+
+template <bool BF16>
+struct SweepLds {
+  static constexpr int SP = BF16 ? 2 : 3, SV = BF16 ? 1 : 3;
+  static constexpr int kK = 0;                      // decayed keys [i][c]
+  static constexpr int kV = kK + SP * PL * 2;       // V^T [n][t]
+  static constexpr int kS = kV + SV * PL * 2;       // S^T [n][c]
+  static constexpr int kBT = kS + SP * PL * 2;      // block totals [4][64]
+  static constexpr int kU = kBT + 4 * 64 * 4;
+  static constexpr int kFlag = kU + 64 * 4;
+  static constexpr int kBytes = kFlag + 16;
+};
+
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -172,60 +185,6 @@ __device__ __forceinline__ f32x4 mma(const Op<SA>& a, const Op<SB>& b, f32x4 c) 
 // ---- 64x64 bf16 planes in LDS, 16-byte chunks XOR-swizzled by row
 __device__ __forceinline__ int swz(int row, int col) {
   return row * 64 + ((((col >> 3) ^ (row & 7)) << 3) | (col & 7));
-}
-
-template <int S>
-__device__ __forceinline__ Op<S> lds_read8(const __bf16* P, int row, int col0) {
-  Op<S> o;
-#pragma unroll
-  for (int s = 0; s < S; ++s) o.p[s] = *reinterpret_cast<const bf16x8*>(P + s * PL + swz(row, col0));
-  return o;
-}
-
-// slots 0..3 from columns c0..c0+3, slots 4..7 from columns c1..c1+3
-template <int S>
-__device__ __forceinline__ Op<S> lds_read4x2(const __bf16* P, int row, int c0, int c1) {
-  Op<S> o;
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(P + s * PL + swz(row, c0));
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(P + s * PL + swz(row, c1));
-    o.p[s] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  }
-  return o;
-}
-
-template <int S>
-__device__ __forceinline__ void lds_write8(__bf16* P, int row, int col0, const float* x) {
-  const Op<S> o = split8<S>(x);
-#pragma unroll
-  for (int s = 0; s < S; ++s) *reinterpret_cast<bf16x8*>(P + s * PL + swz(row, col0)) = o.p[s];
-}
-
-template <int S>
-__device__ __forceinline__ void lds_write4(__bf16* P, int row, int col0, const float* x) {
-  float r[4] = {x[0], x[1], x[2], x[3]};
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    bf16x4 q;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const __bf16 h = (__bf16)r[j];
-      q[j] = h;
-      r[j] -= (float)h;
-    }
-    *reinterpret_cast<bf16x4*>(P + s * PL + swz(row, col0)) = q;
-  }
-}
-
-template <int S>
-__device__ __forceinline__ void lds_write1(__bf16* P, int row, int col, float x) {
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const __bf16 h = (__bf16)x;
-    P[s * PL + swz(row, col)] = h;
-    x -= (float)h;
-  }
 }
 
 // Lane offsets into the swizzled planes, computed once per kernel so that
@@ -320,31 +279,6 @@ __device__ __forceinline__ void wr1(__bf16* P, int off, float x) {
   }
 }
 
-// ---- split planes in global memory (row-major, unswizzled)
-template <int S>
-__device__ __forceinline__ Op<S> gl_read8(const __bf16* P, int row, int col0) {
-  Op<S> o;
-#pragma unroll
-  for (int s = 0; s < S; ++s) o.p[s] = *reinterpret_cast<const bf16x8*>(P + s * PL + row * 64 + col0);
-  return o;
-}
-
-template <int S>
-__device__ __forceinline__ void gl_write4(__bf16* P, int row, int col0, const float* x) {
-  float r[4] = {x[0], x[1], x[2], x[3]};
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    bf16x4 q;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const __bf16 h = (__bf16)r[j];
-      q[j] = h;
-      r[j] -= (float)h;
-    }
-    *reinterpret_cast<bf16x4*>(P + s * PL + row * 64 + col0) = q;
-  }
-}
-
 // ---- input rows: the 16 home elements of a lane (channels 8g.. and 32+8g..)
 template <bool BF16>
 struct Raw {
@@ -366,27 +300,6 @@ __device__ __forceinline__ Raw<BF16> gload(const void* base, int64_t row_off, in
     r.q[3] = *reinterpret_cast<const uint4*>(p + 32 + 8 * g + 4);
   }
   return r;
-}
-
-template <bool BF16>
-__device__ __forceinline__ Raw<BF16> rzero() {
-  Raw<BF16> r;
-#pragma unroll
-  for (int i = 0; i < (BF16 ? 2 : 4); ++i) r.q[i] = make_uint4(0u, 0u, 0u, 0u);
-  return r;
-}
-
-// Zero the raw words of a row that lies past the end of the sequence (the
-// loads themselves are unconditional: they read a clamped, valid row).
-template <bool BF16>
-__device__ __forceinline__ void mask_row(Raw<BF16>& r, bool valid) {
-#pragma unroll
-  for (int i = 0; i < (BF16 ? 2 : 4); ++i) {
-    r.q[i].x = valid ? r.q[i].x : 0u;
-    r.q[i].y = valid ? r.q[i].y : 0u;
-    r.q[i].z = valid ? r.q[i].z : 0u;
-    r.q[i].w = valid ? r.q[i].w : 0u;
-  }
 }
 
 template <bool BF16>
@@ -547,18 +460,6 @@ __device__ __forceinline__ void zero_rows16(__bf16* P, int t0, int lane) {
       *reinterpret_cast<uint4*>(P + s * PL + swz(row, cb + 8 * hq)) = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Column read of a split plane set: k-slots j = 0..7 are rows r0 + j of
-// column col (an A operand whose K dimension runs down the stored rows).
-template <int S>
-__device__ __forceinline__ Op<S> lds_read_col8(const __bf16* P, int r0, int col) {
-  Op<S> o;
-#pragma unroll
-  for (int s = 0; s < S; ++s)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o.p[s][j] = P[s * PL + swz(r0 + j, col)];
-  return o;
-}
-
 template <int S>
 __device__ __forceinline__ void join8(const Op<S>& o, float (&x)[8]) {
 #pragma unroll
@@ -589,669 +490,611 @@ __device__ __forceinline__ void unpack_half(const Raw<BF16>& r, int ks, float (&
   }
 }
 
-// ---------------------------------------------------------------------------
-// Segment pre-pass: one workgroup per (batch, head, segment); sweeps the
-// segment's chunks from last to first.  The state each chunk receives from
-// the later chunks of its segment is stored split, multiplied by the chunk's
-// own total decay 2^Ltot when the chunk takes the fast path (the forward
-// kernel then pairs it with the query r 2^(-Lin)), unscaled otherwise.
-template <bool BF16, bool BIDIR, bool CARRY>
-__global__ __launch_bounds__(NT, BF16 ? 2 : 1) void seg_kernel(Params p) {
+// Half ks of a raw row as floats, zero for a token past the sequence end
+// (the loads read a clamped, valid row; its values must not leak into keys).
+template <bool BF16>
+__device__ __forceinline__ void unpack_half_masked(const Raw<BF16>& r, int ks, bool valid, float (&o)[8]) {
+  unpack_half<BF16>(r, ks, o);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = valid ? o[j] : 0.f;
+}
+
+// V^T columns of the lane's token: element (32 ks + 8 g + j, tau) for its 16
+// home channels; zero for a token past the sequence end.  bf16 values are
+// stored as they were read.
+template <bool BF16>
+__device__ __forceinline__ void write_vT(__bf16* sV, const int (&c)[8], const Raw<BF16>& r, bool valid) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if constexpr (BF16) {
+      const uint4 q = r.q[ks];
+      const uint32_t w4[4] = {valid ? q.x : 0u, valid ? q.y : 0u, valid ? q.z : 0u, valid ? q.w : 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sV[2048 * ks + c[2 * j]] = __builtin_bit_cast(__bf16, (unsigned short)(w4[j] & 0xFFFFu));
+        sV[2048 * ks + c[2 * j + 1]] = __builtin_bit_cast(__bf16, (unsigned short)(w4[j] >> 16));
+      }
+    } else {
+      float v[8];
+      unpack_half_masked<BF16>(r, ks, valid, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wr1<3>(sV, 2048 * ks + c[j], v[j]);
+    }
+  }
+}
+
+
+
+// A chunk in which some 16-token block decays by 2^-kBlockSpan or more:
+// phases B and C with references at the key blocks' own boundaries.  Past
+// keys of block J carry k 2^(E_J - Lin) (E_I: prefix at the end of block I);
+// the queries r 2^(Lex - E_I) of each key block and r 2^Lex of the state
+// product are built in phase C from the raw r and w words.
+template <bool BF16, int MODE, bool DIAG>
+__device__ __forceinline__ void slow_chunk(const Params& p, char* lds, Raw<BF16> rraw, Raw<BF16> kraw,
+                                                     Raw<BF16> wraw, int64_t yoff, int Lv, bool left) {
   constexpr int SP = BF16 ? 2 : 3;
   constexpr int SV = BF16 ? 1 : 3;
-  __shared__ __attribute__((aligned(16))) __bf16 sEb[BIDIR ? SP * PL : 8];   // (k 2^Lex)^T   [c][t]
-  __shared__ __attribute__((aligned(16))) __bf16 sEf[CARRY ? SP * PL : 8];   // (k 2^(Ltot-Lin+D))^T
-  __shared__ __attribute__((aligned(16))) __bf16 sV[SV * PL];                 // V^T [n][t]
-  __shared__ __attribute__((aligned(16))) float sBT[4 * 64];
-  __shared__ __attribute__((aligned(16))) int sFlag[4];
-
+  constexpr bool OUT = MODE != kState;
+  using L = SweepLds<BF16>;
+  __bf16* sK = reinterpret_cast<__bf16*>(lds + L::kK);
+  __bf16* sV = reinterpret_cast<__bf16*>(lds + L::kV);
+  __bf16* sS = reinterpret_cast<__bf16*>(lds + L::kS);
+  float* sBT = reinterpret_cast<float*>(lds + L::kBT);
+  float* sU = reinterpret_cast<float*>(lds + L::kU);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int J = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
   const int tau = 16 * J + li;
   const LdsOff lo = lds_offsets(J, g, li);
-  const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
-  const int b = bh / p.H, h = bh % p.H;
-  const int64_t T = p.T, C = p.C;
-  const int64_t base = (int64_t)b * T * C + (int64_t)h * HS;
-  const int c0 = seg * p.CPS;
-  const int c1 = min(p.NC, c0 + p.CPS);   // chunks [c0, c1)
+  const bool valid = tau < Lv;
+  const bool active = 16 * J < Lv;
+  float lin[2][8];
+  if (active) block_scan<BF16>(wraw, valid, lin);
 
-  f32x4 Sb[4], F[4];   // rows 16J + 4g + j, columns 16 nt + li
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) Sb[nt] = F[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float D[2][8];       // log2 decay from the end of the current chunk to the segment end
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) D[ks][j] = 0.f;
-
-  // buffers: [0] k, [1] v, [2] w.  Loads are unconditional (rows clamped to
-  // the sequence) so the compiler can keep them in flight across the chunk.
-  auto fetch = [&](int ch, Raw<BF16> (&buf)[3]) {
-    const int64_t t = min((int64_t)ch * LC + tau, T - 1);
-    const int64_t off = base + t * C;
-    buf[0] = gload<BF16>(p.k, off, g);
-    buf[1] = gload<BF16>(p.v, off, g);
-    buf[2] = gload<BF16>(p.w, off, g);
-  };
-
-  auto body = [&](int ch, Raw<BF16> (&cur)[3], Raw<BF16> (&nxt)[3]) __attribute__((always_inline)) {
-    const int Lv = (int)min<int64_t>(LC, T - (int64_t)ch * LC);
-    const bool valid = tau < Lv;
-    const bool active = 16 * J < Lv;   // uniform in the wave
-    lds_barrier();
-    fetch(max(ch - 1, c0), nxt);
-
-    // ---- phase A: scan, block totals, values
-    float lin[2][8];
-    if (active) {
-      if (Lv < LC) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) mask_row<BF16>(cur[i], valid);
-      }
-      block_scan<BF16>(cur[2], valid, lin);
-      publish_block(lin, sBT, sFlag, J, g, li, lane);
-      float v[8];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        unpack_half<BF16>(cur[1], ks, v);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wr1<SV>(sV, 2048 * ks + lo.c[j], v[j]);
-      }
-    } else {
-      publish_empty_block(sBT, sFlag, J, lane);
-      zero_cols16<SV>(sV, 16 * J, lane);
-      if (BIDIR) zero_cols16<SP>(sEb, 16 * J, lane);
-      if (CARRY) zero_cols16<SP>(sEf, 16 * J, lane);
-    }
-    lds_barrier();
-
-    // ---- phase B: decayed keys, stored transposed
-    const bool slow = chunk_is_slow(sFlag);
+  // ---- phase B (slow)
+  float dg = 0.f;
+  if (active) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int cb = 32 * ks + 8 * g;
-      float tot[8];
-      if (CARRY) {
-        float4 t0, t1;
-        t0 = *reinterpret_cast<const float4*>(&sBT[cb]);
-        t1 = *reinterpret_cast<const float4*>(&sBT[cb + 4]);
-        tot[0] = t0.x; tot[1] = t0.y; tot[2] = t0.z; tot[3] = t0.w;
-        tot[4] = t1.x; tot[5] = t1.y; tot[6] = t1.z; tot[7] = t1.w;
-#pragma unroll
-        for (int I = 1; I < 4; ++I) {
-          float bb[8];
-          load8f(&sBT[I * 64 + cb], bb);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) tot[j] += bb[j];
-        }
+      float off[8], k[8], kf[8];
+      block_offset(sBT, J, cb, off);
+      unpack_half_masked<BF16>(kraw, ks, valid, k);
+      float r[8], uu[8];
+      if (DIAG) {
+        unpack_half<BF16>(rraw, ks, r);
+        load8f(&sU[cb], uu);
       }
-      if (active) {
-        float off[8], k[8];
-        block_offset(sBT, J, cb, off);
-        unpack_half<BF16>(cur[0], ks, k);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (BIDIR) wr1<SP>(sEb, 2048 * ks + lo.c[j], k[j] * ex2(row_shr<1>(lin[ks][j]) + off[j]));
-          if (CARRY) wr1<SP>(sEf, 2048 * ks + lo.c[j], k[j] * ex2(tot[j] - (lin[ks][j] + off[j]) + D[ks][j]));
-        }
+      for (int j = 0; j < 8; ++j) {
+        const float eJ = off[j] + sBT[J * 64 + cb + j];
+        kf[j] = k[j] * ex2(eJ - (lin[ks][j] + off[j]));
+        if (DIAG) dg += r[j] * uu[j] * k[j];
       }
-      if (CARRY) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) D[ks][j] += tot[j];
-      }
+      wr8<SP>(sK, 1024 * J + lo.a[ks], kf);
     }
-    lds_barrier();
+    if (DIAG) {
+      dg += __shfl_xor(dg, 16);
+      dg += __shfl_xor(dg, 32);
+    }
+  }
+  lds_barrier();
 
-    // ---- phase D: state rows 16J + 4g + j
-    float tot4[4], dec[4];
-    chunk_total4(sBT, 16 * J + 4 * g, tot4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dec[j] = ex2(tot4[j]);
-    // state each chunk receives from the later chunks of the segment
-    if (BIDIR && ch < c1 - 1) {
-      __bf16* dst = p.rev + ((int64_t)bh * p.NC + ch) * (SP * PL);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        float x[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = slow ? Sb[nt][j] : Sb[nt][j] * dec[j];
-        gl_write4<SP>(dst, 16 * nt + li, 16 * J + 4 * g, x);
-      }
-    }
-    // Sb <- 2^Ltot Sb + (k 2^Lex)^T V ;  F += (k 2^(Ltot - Lin + D))^T V
-    if (BIDIR) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Sb[nt][j] *= dec[j];
-    }
+  // ---- phase C (slow)
+  if (OUT && active) {
+    // Lin and Lex of the lane's elements, rebuilt from the raw w words
+    float lns[2][8], lxs[2][8];
+    block_scan<BF16>(wraw, valid, lns);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      if (32 * ks >= Lv) break;
-      Op<SP> eb, ef;
-      if (BIDIR) eb = rd8<SP>(sEb, 1024 * J + lo.a[ks]);
-      if (CARRY) ef = rd8<SP>(sEf, 1024 * J + lo.a[ks]);
+      float off[8];
+      block_offset(sBT, J, 32 * ks + 8 * g, off);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const Op<SV> vb = rd8<SV>(sV, 1024 * nt + lo.a[ks]);
-        if (BIDIR) Sb[nt] = mma(eb, vb, Sb[nt]);
-        if (CARRY) F[nt] = mma(ef, vb, F[nt]);
+      for (int j = 0; j < 8; ++j) {
+        lxs[ks][j] = row_shr<1>(lns[ks][j]) + off[j];
+        lns[ks][j] += off[j];
       }
     }
-  };
-
-  Raw<BF16> X[3], Y[3];
-  fetch(c1 - 1, X);
-  for (int ch = c1 - 1; ch >= c0; ch -= 2) {
-    body(ch, X, Y);
-    if (ch - 1 >= c0) body(ch - 1, Y, X);
-  }
-
-  if (CARRY) {
-    float* dst = p.summ + ((int64_t)bh * p.G + seg) * kSummFloats;
+    f32x4 Y[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = 16 * nt + li;
-      *reinterpret_cast<float4*>(dst + n * HS + 16 * J + 4 * g) = make_float4(F[nt][0], F[nt][1], F[nt][2], F[nt][3]);
-      *reinterpret_cast<float4*>(dst + PL + n * HS + 16 * J + 4 * g) =
-          make_float4(Sb[nt][0], Sb[nt][1], Sb[nt][2], Sb[nt][3]);
+    for (int nt = 0; nt < 4; ++nt) Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (left) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float r[8], qv[8];
+        unpack_half<BF16>(rraw, ks, r);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qv[j] = r[j] * ex2(lxs[ks][j]);
+        const Op<SP> qo = split8<SP>(qv);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) Y[nt] = mma(rd8<SP>(sS, 1024 * nt + lo.a[ks]), qo, Y[nt]);
+      }
     }
-    if (J == 0 && li == 0) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+    for (int pr = 0; pr < 2; ++pr) {
+      const int I0 = 2 * pr;
+      if (I0 > J) break;
+      float mx[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dst[2 * PL + 32 * ks + 8 * g + j] = D[ks][j];
+      for (int hh = 0; hh < 2; ++hh) {
+        const int I = I0 + hh;
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        if (I <= J) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            float e[8], r[8], qv[8];
+            block_end8(sBT, I, 32 * ks + 8 * g, e);
+            unpack_half<BF16>(rraw, ks, r);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qv[j] = r[j] * ex2(lxs[ks][j] - e[j]);
+            a = mma(rd8<SP>(sK, 1024 * I + lo.a[ks]), split8<SP>(qv), a);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * I + 4 * g + j;
+          float val = (i < tau) ? a[j] : 0.f;
+          if (DIAG) val += (i == tau) ? dg : 0.f;
+          mx[4 * hh + j] = val;
+        }
+      }
+      const Op<SP> mo = split8<SP>(mx);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        Y[nt] = mma(rd4x2<SV>(sV, 1024 * nt + lo.v[pr][0], 1024 * nt + lo.v[pr][1]), mo, Y[nt]);
+    }
+    if (valid) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float4 o = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
+        if (MODE == kOutAcc) {
+          const float4 yo = *reinterpret_cast<const float4*>(p.y + yoff + 16 * nt + 4 * g);
+          o.x += yo.x;
+          o.y += yo.y;
+          o.z += yo.z;
+          o.w += yo.w;
+        }
+        *reinterpret_cast<float4*>(p.y + yoff + 16 * nt + 4 * g) = o;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Main sweep: outputs of one segment, left to right.
-template <bool BF16, bool BIDIR, bool CARRY>
-__global__ __launch_bounds__(NT, BF16 ? 2 : 1) void fwd_kernel(Params p) {
+// One sweep of one segment in one direction.  Sweep position q runs over the
+// segment's tokens in sweep order (REV: from its last token down), so the
+// reverse sum of the bidirectional mode is the causal sum of the reversed
+// sequence without the u term, and both directions share this code.
+//   MODE kState:  no outputs; writes the segment's end state and total log2
+//                 decay (started from zero) to the summaries.
+//   MODE kOut:    y = the sweep's outputs.
+//   MODE kOutAcc: y += the sweep's outputs (y holds the reverse sweep's part).
+//   CARRY:        start from the state the earlier segments (in sweep order)
+//                 hand over, combined from their summaries.
+template <bool BF16, bool REV, int MODE, bool CARRY, bool SLOW>
+__device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int seg) {
   constexpr int SP = BF16 ? 2 : 3;
   constexpr int SV = BF16 ? 1 : 3;
-  constexpr bool RIN = BIDIR && CARRY;
-  __shared__ __attribute__((aligned(16))) __bf16 sKf[SP * PL];              // keys, past tokens [i][c]
-  __shared__ __attribute__((aligned(16))) __bf16 sKb[BIDIR ? SP * PL : 8];  // keys, later tokens [i][c]
-  __shared__ __attribute__((aligned(16))) __bf16 sV[SV * PL];               // V^T [n][t]
-  __shared__ __attribute__((aligned(16))) __bf16 sS[SP * PL];               // S^T [n][c]
-  __shared__ __attribute__((aligned(16))) __bf16 sSr[BIDIR ? SP * PL : 8];  // S'^T [n][c] entering this chunk
-  __shared__ __attribute__((aligned(16))) float sBT[4 * 64];
-  __shared__ __attribute__((aligned(16))) float sU[64];
-  __shared__ __attribute__((aligned(16))) int sFlag[4];
+  constexpr bool OUT = MODE != kState;
+  constexpr bool DIAG = OUT && !REV;   // the u term belongs to the forward sweep
+  using L = SweepLds<BF16>;
+  __bf16* sK = reinterpret_cast<__bf16*>(lds + L::kK);
+  __bf16* sV = reinterpret_cast<__bf16*>(lds + L::kV);
+  __bf16* sS = reinterpret_cast<__bf16*>(lds + L::kS);
+  float* sBT = reinterpret_cast<float*>(lds + L::kBT);
+  float* sU = reinterpret_cast<float*>(lds + L::kU);
+  int* sFlag = reinterpret_cast<int*>(lds + L::kFlag);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int J = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
-  const int tau = 16 * J + li;   // home token of the lane (also its output column)
+  const int tau = 16 * J + li;   // the lane's position in the chunk (also its output column)
   const LdsOff lo = lds_offsets(J, g, li);
-  const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
   const int b = bh / p.H, h = bh % p.H;
   const int64_t T = p.T, C = p.C;
   const int64_t base = (int64_t)b * T * C + (int64_t)h * HS;
-  const int c0 = seg * p.CPS;
-  const int c1 = min(p.NC, c0 + p.CPS);
+  const int64_t t_lo = (int64_t)seg * p.SEGC * LC;
+  const int64_t t_hi = min(T, t_lo + (int64_t)p.SEGC * LC);
+  const int64_t n = t_hi - t_lo;
+  const int nch = (int)((n + LC - 1) / LC);
+  auto token = [&](int64_t q) { return REV ? t_hi - 1 - q : t_lo + q; };
 
-  if (tid < 64) sU[tid] = p.u[h * HS + tid];   // read after the first barrier
+  if (DIAG && tid < 64) sU[tid] = p.u[h * HS + tid];   // read after the first barrier
 
-  // ---- carries from the other segments
-  f32x4 S[4];   // S[16J + 4g + j][16 nt + li]
+  // ---- state, rows 16J + 4g + j, columns 16 nt + li
+  f32x4 S[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // State from the later segments, for the staging elements of this thread
-  // (row tid / 4, columns 16 (tid % 4) .. + 15 of S'^T), and the log2 decay
-  // from the current chunk's start to the end of this segment for those columns.
-  float Rr[RIN ? 16 : 1], rf[RIN ? 16 : 1];
-#pragma unroll
-  for (int j = 0; j < (RIN ? 16 : 1); ++j) Rr[j] = rf[j] = 0.f;
-  const int srow = tid >> 2, scol = 16 * (tid & 3);
-  bool have_S = false, have_R = false;
+  bool have_S = false;
   if (CARRY) {
-    const float* sm = p.summ + (int64_t)bh * p.G * kSummFloats;
-    for (int s2 = 0; s2 < seg; ++s2) {
-      const float* Fs = sm + (int64_t)s2 * kSummFloats;
+    // (g1, S1) o (g2, S2) = (g1 + g2, 2^g2 S1 + S2) over the earlier segments
+    const int nprev = REV ? p.G - 1 - seg : seg;
+    for (int k2 = 0; k2 < nprev; ++k2) {
+      const int s2 = REV ? p.G - 1 - k2 : k2;
+      const float* Ss = p.summ + (((int64_t)bh * p.G + s2) * 2 + (REV ? 1 : 0)) * kSummFloats;
+      float gj[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gj[j] = ex2(Ss[PL + 16 * J + 4 * g + j]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const float4 f = *reinterpret_cast<const float4*>(Fs + (16 * nt + li) * HS + 16 * J + 4 * g);
-        const float fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[nt][j] = S[nt][j] * ex2(Fs[2 * PL + 16 * J + 4 * g + j]) + fv[j];
+        const float4 f = *reinterpret_cast<const float4*>(Ss + (16 * nt + li) * HS + 16 * J + 4 * g);
+        S[nt][0] = S[nt][0] * gj[0] + f.x;
+        S[nt][1] = S[nt][1] * gj[1] + f.y;
+        S[nt][2] = S[nt][2] * gj[2] + f.z;
+        S[nt][3] = S[nt][3] * gj[3] + f.w;
       }
     }
-    have_S = seg > 0;
-    if (have_S) {
+    have_S = nprev > 0;
+    if (OUT && have_S) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
         wr4<SP>(sS, 1024 * nt + lo.s, x);
       }
     }
-    if (RIN) {
-      have_R = seg < p.G - 1;
-      if (have_R) {
-        for (int s2 = p.G - 1; s2 > seg; --s2) {
-          const float* Rs = sm + (int64_t)s2 * kSummFloats + PL;
-          const float* gs = sm + (int64_t)s2 * kSummFloats + 2 * PL;
-#pragma unroll
-          for (int j = 0; j < (RIN ? 16 : 1); ++j) Rr[j] = Rr[j] * ex2(gs[scol + j]) + Rs[srow * HS + scol + j];
-        }
-        const float* gseg = sm + (int64_t)seg * kSummFloats + 2 * PL;
-#pragma unroll
-        for (int j = 0; j < (RIN ? 16 : 1); ++j) rf[j] = gseg[scol + j];
-      }
-    }
   }
+  float gsum[4] = {0.f, 0.f, 0.f, 0.f};   // kState: total log2 decay of the state rows
 
-  // Per-chunk global data: [0] r, [1] k, [2] v, [3] w rows of the lane's home
-  // token, and 2 SP 16-byte pieces of the chunk's reverse-state tile (thread t
-  // holds row t / 4, columns 16 (t % 4) .. + 15 of each plane).  The next
-  // chunk's loads are issued once the current chunk's operands are built and
-  // stay in flight through the contractions.  Rows and chunks are clamped to
-  // valid memory so the loads are unconditional.
-  struct Buf {
-    Raw<BF16> in[4];
-    uint4 sr[BIDIR ? 2 * SP : 1];
+  // Raw rows of the lane's token for the chunk: [0] r, [1] k, [2] v, [3] w.
+  // The next chunk's loads are issued after the current chunk's outputs (the
+  // other resident workgroups cover their latency); rows are clamped into the
+  // segment so the loads are unconditional.
+  Raw<BF16> buf[4];
+  auto fetch = [&](int ch) {
+    const int64_t q = min((int64_t)ch * LC + tau, n - 1);
+    const int64_t off = base + token(q) * C;
+    if (OUT) buf[0] = gload<BF16>(p.r, off, g);
+    buf[1] = gload<BF16>(p.k, off, g);
+    buf[2] = gload<BF16>(p.v, off, g);
+    buf[3] = gload<BF16>(p.w, off, g);
   };
-  auto fetch = [&](int ch, Buf& buf) {
-    const int64_t t = min((int64_t)ch * LC + tau, T - 1);
-    const int64_t off = base + t * C;
-    buf.in[0] = gload<BF16>(p.r, off, g);
-    buf.in[1] = gload<BF16>(p.k, off, g);
-    buf.in[2] = gload<BF16>(p.v, off, g);
-    buf.in[3] = gload<BF16>(p.w, off, g);
-    if constexpr (BIDIR) {
-      const __bf16* src = p.rev + ((int64_t)bh * p.NC + ch) * (SP * PL) + srow * 64 + scol;
-#pragma unroll
-      for (int s = 0; s < SP; ++s) {
-        buf.sr[2 * s] = *reinterpret_cast<const uint4*>(src + s * PL);
-        buf.sr[2 * s + 1] = *reinterpret_cast<const uint4*>(src + s * PL + 8);
-      }
-    }
-  };
-  Buf buf;
-  fetch(c0, buf);
+  fetch(0);
 
-  for (int ch = c0; ch < c1; ++ch) {
-    const int64_t s0 = (int64_t)ch * LC;
-    const int Lv = (int)min<int64_t>(LC, T - s0);
+  // Chunks run on the fast path until the first chunk that needs the slow
+  // one; from there on every chunk takes the slow path (it is valid for any
+  // chunk), so that neither loop carries the other's registers.
+  int ch = 0;
+  for (; ch < nch; ++ch) {
+    const int Lv = (int)min<int64_t>(LC, n - (int64_t)ch * LC);
     const bool valid = tau < Lv;
     const bool active = 16 * J < Lv;   // uniform in the wave
-    const bool left = ch > c0 || have_S;
-    const bool right = BIDIR && (ch < c1 - 1 || have_R);
+    const bool left = ch > 0 || have_S;
     lds_barrier();
 
     // ---- phase A: in-block scan, block totals, values
     float lin[2][8];
     if (active) {
-      if (Lv < LC) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mask_row<BF16>(buf.in[i], valid);
-      }
-      block_scan<BF16>(buf.in[3], valid, lin);
+      block_scan<BF16>(buf[3], valid, lin);
       publish_block(lin, sBT, sFlag, J, g, li, lane);
-      float v[8];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        unpack_half<BF16>(buf.in[2], ks, v);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wr1<SV>(sV, 2048 * ks + lo.c[j], v[j]);
-      }
+      write_vT<BF16>(sV, lo.c, buf[2], valid);
     } else {
       publish_empty_block(sBT, sFlag, J, lane);
       zero_cols16<SV>(sV, 16 * J, lane);
-      zero_rows16<SP>(sKf, 16 * J, lane);
-      if (BIDIR) zero_rows16<SP>(sKb, 16 * J, lane);
+      zero_rows16<SP>(sK, 16 * J, lane);
+    }
+    lds_barrier();
+    if (chunk_is_slow(sFlag)) break;   // uniform: every wave reads the same flags
+
+    // ---- phase B (fast): keys k 2^(-Lin) to LDS; queries r 2^Lex split in
+    // registers; bonus diagonal.  The output accumulators start from the
+    // rows of y the reverse sweep left (kOutAcc) or from zero.
+    Op<SP> q[2];
+    float dg = 0.f;
+    const int64_t yoff = base + token((int64_t)ch * LC + tau) * C;
+    f32x4 Y[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (MODE == kOutAcc && valid) {
+        const float4 yo = *reinterpret_cast<const float4*>(p.y + yoff + 16 * nt + 4 * g);
+        Y[nt] = f32x4{yo.x, yo.y, yo.z, yo.w};
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int cb = 32 * ks + 8 * g;
+        float off[8], k[8], kf[8];
+        block_offset(sBT, J, cb, off);
+        unpack_half_masked<BF16>(buf[1], ks, valid, k);
+        float r[8], uu[8], qf[8];
+        if (OUT) unpack_half<BF16>(buf[0], ks, r);
+        if (DIAG) load8f(&sU[cb], uu);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          kf[j] = k[j] * ex2(-(lin[ks][j] + off[j]));
+          if (OUT) qf[j] = r[j] * ex2(row_shr<1>(lin[ks][j]) + off[j]);
+          if (DIAG) dg += r[j] * uu[j] * k[j];
+        }
+        wr8<SP>(sK, 1024 * J + lo.a[ks], kf);
+        if (OUT) q[ks] = split8<SP>(qf);
+      }
+      if (DIAG) {
+        dg += __shfl_xor(dg, 16);
+        dg += __shfl_xor(dg, 32);
+      }
     }
     lds_barrier();
 
-    const bool slow = chunk_is_slow(sFlag);
-    // ---- phase B0: state entering this chunk from the right: the later
-    // chunks of the segment (prefetched, pre-split) plus, with segments, R of
-    // the later segments decayed to this chunk
-    if (BIDIR) {
-      if (!RIN || !have_R) {
-        if (ch < c1 - 1) {
+    // ---- phase C (fast): scores of the key blocks up to the lane's own,
+    // outputs
+    if (OUT && active) {
 #pragma unroll
-          for (int s = 0; s < SP; ++s) {
-            *reinterpret_cast<uint4*>(sSr + s * PL + swz(srow, scol)) = buf.sr[2 * s];
-            *reinterpret_cast<uint4*>(sSr + s * PL + swz(srow, scol + 8)) = buf.sr[2 * s + 1];
+      for (int pr = 0; pr < 2; ++pr) {
+        const int I0 = 2 * pr;
+        if (I0 > J) break;
+        float mx[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int I = I0 + hh;
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+          if (I <= J) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) a = mma(rd8<SP>(sK, 1024 * I + lo.a[ks]), q[ks], a);
           }
-        }
-      } else {
-        float x[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = 0.f;
-        if (ch < c1 - 1) {
-#pragma unroll
-          for (int s = 0; s < SP; ++s)
-#pragma unroll
-            for (int hq = 0; hq < 2; ++hq) {
-              const uint4 q = buf.sr[2 * s + hq];
-              const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                x[8 * hq + 2 * j] += __uint_as_float(w4[j] << 16);
-                x[8 * hq + 2 * j + 1] += __uint_as_float(w4[j] & 0xFFFF0000u);
-              }
-            }
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float t2[4];
-          chunk_total4(sBT, scol + 4 * q4, t2);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int jj = 4 * q4 + j;
-            // fast: the query carries 2^(-Lin), so R enters with the decay from
-            // the chunk start; slow: the query carries 2^(Ltot - Lin)
-            const float before = rf[jj];
-            rf[jj] -= t2[j];
-            x[jj] += ex2(slow ? rf[jj] : before) * Rr[jj];
+            const int i = 16 * I + 4 * g + j;
+            float val;
+            if (I < J) val = a[j];
+            else if (I > J) val = 0.f;
+            else val = i < tau ? a[j] : ((DIAG && i == tau) ? dg : 0.f);
+            mx[4 * hh + j] = val;
           }
         }
-        lds_write8<SP>(sSr, srow, scol, x);
-        lds_write8<SP>(sSr, srow, scol + 8, x + 8);
+        const Op<SP> mo = split8<SP>(mx);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          Y[nt] = mma(rd4x2<SV>(sV, 1024 * nt + lo.v[pr][0], 1024 * nt + lo.v[pr][1]), mo, Y[nt]);
+      }
+      // Y^T += S^T (r 2^Lex)^T : state from the earlier chunks
+      if (left) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) Y[nt] = mma(rd8<SP>(sS, 1024 * nt + lo.a[ks]), q[ks], Y[nt]);
+      }
+      if (valid) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          *reinterpret_cast<float4*>(p.y + yoff + 16 * nt + 4 * g) = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
       }
     }
-
-    if (!slow) {
-      // ---- phase B (fast): keys k 2^(-Lin) (past) and k 2^Lex (later) to LDS;
-      // queries r 2^Lex and r 2^(-Lin) kept split in registers; bonus diagonal
-      Op<SP> rq[2], rbq[2];
-      float dg = 0.f;
-      if (active) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int cb = 32 * ks + 8 * g;
-          float off[8], r[8], k[8], uu[8];
-          block_offset(sBT, J, cb, off);
-          unpack_half<BF16>(buf.in[0], ks, r);
-          unpack_half<BF16>(buf.in[1], ks, k);
-          load8f(&sU[cb], uu);
-          float kf[8], kb[8], qf[8], qb[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float Fc = ex2(-(lin[ks][j] + off[j]));
-            const float Ec = ex2(row_shr<1>(lin[ks][j]) + off[j]);
-            kf[j] = k[j] * Fc;
-            kb[j] = k[j] * Ec;
-            qf[j] = r[j] * Ec;
-            qb[j] = r[j] * Fc;
-            dg += r[j] * uu[j] * k[j];
-          }
-          wr8<SP>(sKf, 1024 * J + lo.a[ks], kf);
-          if (BIDIR) wr8<SP>(sKb, 1024 * J + lo.a[ks], kb);
-          rq[ks] = split8<SP>(qf);
-          if (BIDIR) rbq[ks] = split8<SP>(qb);
-        }
-        dg += __shfl_xor(dg, 16);
-        dg += __shfl_xor(dg, 32);
-      }
-      fetch(min(ch + 1, c1 - 1), buf);
-      lds_barrier();
-
-      // ---- phase C (fast): scores, outputs
-      if (active) {
-        f32x4 Y[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const int I0 = 2 * pr;
-          if ((!BIDIR && I0 > J) || 16 * I0 >= Lv) break;
-          float mx[8];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int I = I0 + hh;
-            f32x4 a = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-            if (16 * I < Lv) {
-              if (I <= J) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) a = mma(rd8<SP>(sKf, 1024 * I + lo.a[ks]), rq[ks], a);
-              }
-              if (BIDIR && I >= J) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) a2 = mma(rd8<SP>(sKb, 1024 * I + lo.a[ks]), rbq[ks], a2);
-              }
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int i = 16 * I + 4 * g + j;
-              float val;
-              if (I < J) val = a[j];
-              else if (I > J) val = a2[j];
-              else val = i < tau ? a[j] : (i > tau ? a2[j] : dg);
-              mx[4 * hh + j] = val;
-            }
-          }
-          const Op<SP> mo = split8<SP>(mx);
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            Y[nt] = mma(rd4x2<SV>(sV, 1024 * nt + lo.v[pr][0], 1024 * nt + lo.v[pr][1]), mo, Y[nt]);
-        }
-        // Y^T += S^T (r 2^Lex)^T : state from the left
-        if (left) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              Y[nt] = mma(rd8<SP>(sS, 1024 * nt + lo.a[ks]), rq[ks], Y[nt]);
-        }
-        // Y^T += S'^T (r 2^(-Lin))^T : state from the right (carries 2^Ltot)
-        if (right) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              Y[nt] = mma(rd8<SP>(sSr, 1024 * nt + lo.a[ks]), rbq[ks], Y[nt]);
-        }
-        if (valid) {
-          float* yrow = p.y + base + (s0 + tau) * C;
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            *reinterpret_cast<float4*>(yrow + 16 * nt + 4 * g) = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
-        }
+    if (ch == nch - 1) {
+      if (OUT) {
+        ch = nch;
+        break;
       }
     } else {
-      // ---- phase B (slow): each key block I uses references at its own
-      // boundaries: past keys k 2^(E_J - Lin) with queries r 2^(Lex - E_I),
-      // later keys k 2^(Lex - B_J) with queries r 2^(B_I - Lin).  The state
-      // products use r 2^Lex and r 2^(Ltot - Lin).  All queries are built in
-      // phase C from the raw r and w words, so the next chunk's loads wait
-      // until phase C is done.
-      float dg = 0.f;
-      if (active) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int cb = 32 * ks + 8 * g;
-          float off[8], r[8], k[8], uu[8];
-          block_offset(sBT, J, cb, off);
-          unpack_half<BF16>(buf.in[0], ks, r);
-          unpack_half<BF16>(buf.in[1], ks, k);
-          load8f(&sU[cb], uu);
-          float kf[8], kb[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int c = cb + j;
-            const float lin_c = lin[ks][j] + off[j];
-            const float lex_c = row_shr<1>(lin[ks][j]) + off[j];
-            const float eJ = off[j] + sBT[J * 64 + c];
-            kf[j] = k[j] * ex2(eJ - lin_c);
-            kb[j] = k[j] * ex2(lex_c - off[j]);
-            dg += r[j] * uu[j] * k[j];
-          }
-          wr8<SP>(sKf, 1024 * J + lo.a[ks], kf);
-          if (BIDIR) wr8<SP>(sKb, 1024 * J + lo.a[ks], kb);
-        }
-        dg += __shfl_xor(dg, 16);
-        dg += __shfl_xor(dg, 32);
-      }
-      lds_barrier();
-
-      // ---- phase C (slow)
-      if (active) {
-        // Lin and Lex of the lane's elements, rebuilt from the raw w words
-        float lns[2][8], lxs[2][8];
-        block_scan<BF16>(buf.in[3], valid, lns);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          float off[8];
-          block_offset(sBT, J, 32 * ks + 8 * g, off);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            lxs[ks][j] = row_shr<1>(lns[ks][j]) + off[j];
-            lns[ks][j] += off[j];
-          }
-        }
-        f32x4 Y[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // state products: S^T (r 2^Lex)^T and S'^T (r 2^(Ltot - Lin))^T
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          float r[8], q[8];
-          unpack_half<BF16>(buf.in[0], ks, r);
-          if (left) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = r[j] * ex2(lxs[ks][j]);
-            const Op<SP> qo = split8<SP>(q);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) Y[nt] = mma(rd8<SP>(sS, 1024 * nt + lo.a[ks]), qo, Y[nt]);
-          }
-          if (right) {
-            float tot[8];
-            block_end8(sBT, 3, 32 * ks + 8 * g, tot);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = r[j] * ex2(tot[j] - lns[ks][j]);
-            const Op<SP> qo = split8<SP>(q);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) Y[nt] = mma(rd8<SP>(sSr, 1024 * nt + lo.a[ks]), qo, Y[nt]);
-          }
-        }
-        // score tiles, key block by key block
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const int I0 = 2 * pr;
-          if ((!BIDIR && I0 > J) || 16 * I0 >= Lv) break;
-          float mx[8];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int I = I0 + hh;
-            f32x4 a = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-            if (16 * I < Lv) {
-              if (I <= J) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                  float e[8], r[8], q[8];
-                  block_end8(sBT, I, 32 * ks + 8 * g, e);
-                  unpack_half<BF16>(buf.in[0], ks, r);
-#pragma unroll
-                  for (int j = 0; j < 8; ++j) q[j] = r[j] * ex2(lxs[ks][j] - e[j]);
-                  a = mma(rd8<SP>(sKf, 1024 * I + lo.a[ks]), split8<SP>(q), a);
-                }
-              }
-              if (BIDIR && I >= J) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                  float e[8], r[8], q[8];
-                  if (I) {
-                    block_end8(sBT, I - 1, 32 * ks + 8 * g, e);
-                  } else {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) e[j] = 0.f;
-                  }
-                  unpack_half<BF16>(buf.in[0], ks, r);
-#pragma unroll
-                  for (int j = 0; j < 8; ++j) q[j] = r[j] * ex2(e[j] - lns[ks][j]);
-                  a2 = mma(rd8<SP>(sKb, 1024 * I + lo.a[ks]), split8<SP>(q), a2);
-                }
-              }
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int i = 16 * I + 4 * g + j;
-              float val = (i < tau) ? a[j] : 0.f;
-              if (BIDIR) val += (i > tau) ? a2[j] : 0.f;
-              val += (i == tau) ? dg : 0.f;
-              mx[4 * hh + j] = val;
-            }
-          }
-          const Op<SP> mo = split8<SP>(mx);
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            Y[nt] = mma(rd4x2<SV>(sV, 1024 * nt + lo.v[pr][0], 1024 * nt + lo.v[pr][1]), mo, Y[nt]);
-        }
-        if (valid) {
-          float* yrow = p.y + base + (s0 + tau) * C;
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            *reinterpret_cast<float4*>(yrow + 16 * nt + 4 * g) = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
-        }
-      }
-      fetch(min(ch + 1, c1 - 1), buf);
+      fetch(ch + 1);
     }
-
-    if (ch == c1 - 1) break;
     lds_barrier();   // every wave has finished reading sS
 
-    // ---- phase D: state rows 16J + 4g + j.  Keys k 2^(-Lin) are read down the
-    // columns of sKf; fast: S <- 2^Ltot (S + K^T V); slow: the keys of token
-    // block I are rescaled to k 2^(Ltot - Lin) and S <- 2^Ltot S + K^T V.
+    // ---- phase D: state rows 16J + 4g + j.  Keys are read down the columns
+    // of sK; fast: S <- 2^Ltot (S + K^T V) with keys k 2^(-Lin); slow: the
+    // keys of token block I are rescaled to k 2^(Ltot - Lin) and
+    // S <- 2^Ltot S + K^T V.
     float tot4[4], dec[4];
     chunk_total4(sBT, 16 * J + 4 * g, tot4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dec[j] = ex2(tot4[j]);
-    if (!slow) {
+    for (int j = 0; j < 4; ++j) {
+      dec[j] = ex2(tot4[j]);
+      if (!OUT) gsum[j] += tot4[j];
+    }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const Op<SP> key = rdcol8<SP>(sKf, lo.c, 2048 * ks);
+    for (int ks = 0; ks < 2; ++ks) {
+      if (32 * ks >= Lv) break;
+      const Op<SP> key = rdcol8<SP>(sK, lo.c, 2048 * ks);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          S[nt] = mma(key, rd8<SV>(sV, 1024 * nt + lo.a[ks]), S[nt]);
+      for (int nt = 0; nt < 4; ++nt) S[nt] = mma(key, rd8<SV>(sV, 1024 * nt + lo.a[ks]), S[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[nt][j] *= dec[j];
+    if (OUT) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
+        wr4<SP>(sS, 1024 * nt + lo.s, x);
       }
-#pragma unroll
+    }
+  }
+
+
+  // ch < nch here: a chunk needs the slow path
+  if constexpr (!SLOW) {
+    if (ch < nch) return false;
+  } else {
+    for (; ch < nch; ++ch) {
+      const int Lv = (int)min<int64_t>(LC, n - (int64_t)ch * LC);
+      const bool valid = tau < Lv;
+      const bool active = 16 * J < Lv;   // uniform in the wave
+      const bool left = ch > 0 || have_S;
+      lds_barrier();
+
+      // ---- phase A: in-block scan, block totals, values
+      float lin[2][8];
+      if (active) {
+        block_scan<BF16>(buf[3], valid, lin);
+        publish_block(lin, sBT, sFlag, J, g, li, lane);
+        write_vT<BF16>(sV, lo.c, buf[2], valid);
+      } else {
+        publish_empty_block(sBT, sFlag, J, lane);
+        zero_cols16<SV>(sV, 16 * J, lane);
+        zero_rows16<SP>(sK, 16 * J, lane);
+      }
+      lds_barrier();
+
+      slow_chunk<BF16, MODE, DIAG>(p, lds, buf[0], buf[1], buf[3], base + token((int64_t)ch * LC + tau) * C, Lv, left);
+      if (ch == nch - 1) {
+        if (OUT) break;
+      } else {
+        fetch(ch + 1);
+      }
+      lds_barrier();   // every wave has finished reading sS
+
+      // ---- phase D: state rows 16J + 4g + j.  Keys are read down the columns
+      // of sK; fast: S <- 2^Ltot (S + K^T V) with keys k 2^(-Lin); slow: the
+      // keys of token block I are rescaled to k 2^(Ltot - Lin) and
+      // S <- 2^Ltot S + K^T V.
+      float tot4[4], dec[4];
+      chunk_total4(sBT, 16 * J + 4 * g, tot4);
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dec[j] = ex2(tot4[j]);
+        if (!OUT) gsum[j] += tot4[j];
+      }
+  #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
+  #pragma unroll
         for (int j = 0; j < 4; ++j) S[nt][j] *= dec[j];
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[nt][j] *= dec[j];
-#pragma unroll
+  #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        Op<SP> key = rdcol8<SP>(sKf, lo.c, 2048 * ks);
+        if (32 * ks >= Lv) break;
+        Op<SP> key = rdcol8<SP>(sK, lo.c, 2048 * ks);
         // rows 32ks + 8g .. + 7 lie in token block I = 2ks + g / 2
         const int c = 16 * J + li;
         const int I = 2 * ks + (g >> 1);
-        const float eI = block_end(sBT, I, c);
-        const float tc = block_end(sBT, 3, c);
+        const float f = ex2(block_end(sBT, 3, c) - block_end(sBT, I, c));
         float x[8];
         join8<SP>(key, x);
-        const float f = ex2(tc - eI);
-#pragma unroll
+  #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] *= f;
         key = split8<SP>(x);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          S[nt] = mma(key, rd8<SV>(sV, 1024 * nt + lo.a[ks]), S[nt]);
+  #pragma unroll
+        for (int nt = 0; nt < 4; ++nt) S[nt] = mma(key, rd8<SV>(sV, 1024 * nt + lo.a[ks]), S[nt]);
+      }
+      if (OUT) {
+  #pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
+          wr4<SP>(sS, 1024 * nt + lo.s, x);
+        }
       }
     }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
-      wr4<SP>(sS, 1024 * nt + lo.s, x);
-    }
   }
+
+  if (!OUT) {
+    float* dst = p.summ + (((int64_t)bh * p.G + seg) * 2 + (REV ? 1 : 0)) * kSummFloats;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      *reinterpret_cast<float4*>(dst + (16 * nt + li) * HS + 16 * J + 4 * g) =
+          make_float4(S[nt][0], S[nt][1], S[nt][2], S[nt][3]);
+    if (li == 0)
+      *reinterpret_cast<float4*>(dst + PL + 16 * J + 4 * g) = make_float4(gsum[0], gsum[1], gsum[2], gsum[3]);
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.  One workgroup of 256 threads per (batch, head[, segment]).
+// Bidirectional calls run the reverse sweep first (it writes y) and then the
+// forward sweep (it adds its part to y) in the same workgroup, so the partial
+// rows are read back from the L2 of the same XCD.
+//
+// Every item first runs with the fast path alone (wkv_kernel,
+// summary_kernel), register-allocated for three resident workgroups per CU.
+// A workgroup that meets a chunk needing the slow path stops and leaves a
+// marker in the first word of its output (y at the segment's first token and
+// the head's first channel, or g[0] of its summary); the fix-up kernel
+// launched next recomputes exactly the marked items with the general sweeps.
+// A marker bit pattern produced by the arithmetic itself (a NaN input that
+// propagates there) only costs a needless recomputation.
+constexpr uint32_t kRedo = 0x7FC0D1A5u;   // quiet NaN with a payload
+
+template <bool BF16>
+constexpr int occupancy() {
+  return BF16 ? 3 : 2;
+}
+
+__device__ __forceinline__ float* item_marker(const Params& p, int bh, int seg) {
+  const int b = bh / p.H, h = bh % p.H;
+  return p.y + ((int64_t)b * p.T + (int64_t)seg * p.SEGC * LC) * p.C + (int64_t)h * HS;
+}
+
+__device__ __forceinline__ float* summary_marker(const Params& p, int bh, int seg, int rev) {
+  return p.summ + (((int64_t)bh * p.G + seg) * 2 + rev) * kSummFloats + PL;
+}
+
+__device__ __forceinline__ void set_marker(float* m) {
+  __syncthreads();   // the workgroup's earlier stores to this word are done
+  if (threadIdx.x == 0) *reinterpret_cast<uint32_t*>(m) = kRedo;
+}
+
+__device__ __forceinline__ bool marker_set(const float* m) {
+  return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(m)) == kRedo;
+}
+
+// Outputs of one item with the sweeps on the fast path (SLOW = false: false
+// as soon as a chunk needs the slow path) or the general sweeps.
+template <bool BF16, bool BIDIR, bool CARRY, bool SLOW>
+__device__ __forceinline__ bool run_item(const Params& p, char* lds, int bh, int seg) {
+  if (BIDIR) {
+    // the forward sweep runs even after the reverse one gave up (its result is
+    // then recomputed anyway): one straight path keeps the registers of the
+    // two sweeps apart
+    const bool ok = sweep<BF16, true, kOut, CARRY, SLOW>(p, lds, bh, seg);
+    __syncthreads();   // partial rows of y written; LDS free for reuse
+    return sweep<BF16, false, kOutAcc, CARRY, SLOW>(p, lds, bh, seg) && ok;
+  }
+  return sweep<BF16, false, kOut, CARRY, SLOW>(p, lds, bh, seg);
+}
+
+template <bool BF16, bool BIDIR, bool CARRY>
+__global__ __launch_bounds__(NT, occupancy<BF16>()) void wkv_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
+  const int bh = CARRY ? blockIdx.x / p.G : blockIdx.x, seg = CARRY ? blockIdx.x % p.G : 0;
+  if (!run_item<BF16, BIDIR, CARRY, false>(p, lds, bh, seg)) set_marker(item_marker(p, bh, seg));
+}
+
+template <bool BF16, bool BIDIR, bool CARRY>
+__global__ __launch_bounds__(NT, 2) void wkv_fixup_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
+  const int bh = CARRY ? blockIdx.x / p.G : blockIdx.x, seg = CARRY ? blockIdx.x % p.G : 0;
+  if (!marker_set(item_marker(p, bh, seg))) return;
+  run_item<BF16, BIDIR, CARRY, true>(p, lds, bh, seg);
+}
+
+// Segment summaries: end state and total decay of each segment in each sweep
+// direction, from a zero state (only those another segment needs).
+template <bool BF16, bool BIDIR>
+__device__ __forceinline__ bool summary_item(int& bh, int& seg, int& rev, const Params& p) {
+  const int dirs = BIDIR ? 2 : 1;
+  bh = blockIdx.x / (p.G * dirs);
+  const int rem = blockIdx.x % (p.G * dirs);
+  seg = rem / dirs;
+  rev = rem % dirs;
+  return rev ? seg > 0 : seg < p.G - 1;
+}
+
+template <bool BF16, bool BIDIR>
+__global__ __launch_bounds__(NT, occupancy<BF16>()) void summary_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
+  int bh, seg, rev;
+  if (!summary_item<BF16, BIDIR>(bh, seg, rev, p)) return;
+  const bool ok = rev ? sweep<BF16, true, kState, false, false>(p, lds, bh, seg)
+                      : sweep<BF16, false, kState, false, false>(p, lds, bh, seg);
+  if (!ok) set_marker(summary_marker(p, bh, seg, rev));
+}
+
+template <bool BF16, bool BIDIR>
+__global__ __launch_bounds__(NT, 2) void summary_fixup_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
+  int bh, seg, rev;
+  if (!summary_item<BF16, BIDIR>(bh, seg, rev, p)) return;
+  if (!marker_set(summary_marker(p, bh, seg, rev))) return;
+  if (rev)
+    sweep<BF16, true, kState, false, true>(p, lds, bh, seg);
+  else
+    sweep<BF16, false, kState, false, true>(p, lds, bh, seg);
 }
 
 struct Plan {
-  int NC, CPS, G;
+  int NC, G, SEGC;
 };
 
 Plan plan(const FwdArgs& a) {
@@ -1262,22 +1105,17 @@ Plan plan(const FwdArgs& a) {
   if (const char* e = getenv("WKV6_SEGMENTS")) {
     G = atoi(e);
   } else {
-    // enough workgroups for every CU: two resident per CU for bf16 inputs
-    const int64_t target = a.bf16 ? 512 : 256;
+    // enough workgroups to fill every CU at the kernel's occupancy
+    const int64_t target = 256 * (a.bf16 ? 3 : 2);
     if (bh < target) G = (int)((target + bh - 1) / bh);
   }
   G = max(1, min(G, pl.NC));
-  pl.CPS = (pl.NC + G - 1) / G;
-  pl.G = (pl.NC + pl.CPS - 1) / pl.CPS;
+  pl.SEGC = (pl.NC + G - 1) / G;
+  pl.G = (pl.NC + pl.SEGC - 1) / pl.SEGC;
   return pl;
 }
 
-template <bool BF16>
-constexpr int planes() {
-  return BF16 ? 2 : 3;
-}
-
-template <bool BF16, bool BIDIR, bool CARRY>
+template <bool BF16, bool BIDIR>
 hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   Params p;
   p.r = a.r;
@@ -1286,47 +1124,50 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   p.w = a.w_raw;
   p.u = a.u;
   p.y = a.y;
-  const size_t rev_bytes = BIDIR ? (size_t)a.B * a.H * pl.NC * planes<BF16>() * PL * sizeof(__bf16) : 0;
-  p.rev = static_cast<__bf16*>(ws);
-  p.summ = CARRY ? reinterpret_cast<float*>(static_cast<char*>(ws) + rev_bytes) : nullptr;
+  p.summ = static_cast<float*>(ws);
   p.T = a.T;
   p.C = a.C;
   p.H = (int)a.H;
-  p.NC = pl.NC;
-  p.CPS = pl.CPS;
   p.G = pl.G;
-  const dim3 grid((unsigned)(a.B * a.H * pl.G)), block(NT);
-  if (BIDIR || CARRY) {
-    hipLaunchKernelGGL((seg_kernel<BF16, BIDIR, CARRY>), grid, block, 0, s, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  p.SEGC = pl.SEGC;
+  const unsigned bh = (unsigned)(a.B * a.H);
+  const dim3 block(NT);
+  hipError_t e;
+  if (pl.G > 1) {
+    const dim3 grid(bh * pl.G * (BIDIR ? 2 : 1));
+    hipLaunchKernelGGL((summary_kernel<BF16, BIDIR>), grid, block, 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((summary_fixup_kernel<BF16, BIDIR>), grid, block, 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((fwd_kernel<BF16, BIDIR, CARRY>), grid, block, 0, s, p);
+  const dim3 grid(bh * pl.G);
+  if (pl.G > 1) {
+    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true>), grid, block, 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, true>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false>), grid, block, 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
-}
-
-template <bool BF16, bool BIDIR>
-hipError_t launch_c(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
-  return pl.G > 1 ? launch_t<BF16, BIDIR, true>(a, pl, ws, s) : launch_t<BF16, BIDIR, false>(a, pl, ws, s);
 }
 
 }  // namespace
 
 size_t workspace_bytes(const FwdArgs& a) {
   const Plan pl = plan(a);
-  size_t n = 0;
-  if (a.bidirectional) n += (size_t)a.B * a.H * pl.NC * (a.bf16 ? 2 : 3) * PL * sizeof(__bf16);
-  if (pl.G > 1) n += (size_t)a.B * a.H * pl.G * kSummFloats * sizeof(float);
-  return n;
+  if (pl.G == 1) return 0;
+  return (size_t)a.B * a.H * pl.G * 2 * kSummFloats * sizeof(float);
 }
 
 hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream) {
   const Plan pl = plan(a);
   if (a.bf16)
-    return a.bidirectional ? launch_c<true, true>(a, pl, workspace, stream)
-                           : launch_c<true, false>(a, pl, workspace, stream);
-  return a.bidirectional ? launch_c<false, true>(a, pl, workspace, stream)
-                         : launch_c<false, false>(a, pl, workspace, stream);
+    return a.bidirectional ? launch_t<true, true>(a, pl, workspace, stream)
+                           : launch_t<true, false>(a, pl, workspace, stream);
+  return a.bidirectional ? launch_t<false, true>(a, pl, workspace, stream)
+                         : launch_t<false, false>(a, pl, workspace, stream);
 }
 
 }  // namespace wkv6
