@@ -8,8 +8,12 @@ outputs rotate over enough copies that no step finds its data in the 256 MB
 Infinity Cache left by the previous steps.
 
 Prints ONE JSON line (rank 0) with, besides the throughput:
-  roofline      achieved HBM bandwidth of the forward kernel(s) from HIP events
-                on the launch stream: algorithmic bytes per call / mean call time
+  roofline      achieved HBM bandwidth of the call from HIP events on the launch
+                stream: algorithmic bytes per call / mean call time (the call is
+                the fast-path sweep kernel plus a fix-up kernel that finds no
+                work unless a chunk needed the slow path, plus the segment
+                summary kernels when a sequence is split); traffic = bytes the
+                committed rocprofv3 counter runs measured for the same sources
   mfma          executed matrix-core work per call and its rate vs the bf16 peak
   cpu_baseline  the float64 CPU oracle timed on the host on a bounded sample
 """
@@ -39,39 +43,76 @@ METRIC = "WKV6 fwd tokens/s (B·T/s) + % HBM roofline & MFMA util at N=64, 1 GPU
 
 
 def kernel_source_hash() -> str:
+    """Hash of the library sources with comments and blank lines stripped, so
+    that a recorded counter run stays matched to the code it measured."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_rnn_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(name.encode() + code.encode())
     return h.hexdigest()[:16]
 
 
+def plan_segments(w: I.Workload) -> tuple[int, int]:
+    """(segments per sequence, chunks per segment) as the library picks them."""
+    nc = math.ceil(w.T / 64)
+    bh = w.B * w.H
+    env = os.environ.get("WKV6_SEGMENTS")
+    if env:
+        g = int(env)
+    else:
+        target = 256 * (3 if w.dtype == "bf16" else 2)
+        g = math.ceil(target / bh) if bh < target else 1
+    g = max(1, min(g, nc))
+    segc = math.ceil(nc / g)
+    return math.ceil(nc / segc), segc
+
+
 def mfma_count(w: I.Workload) -> int:
-    """v_mfma_f32_16x16x32_bf16 instructions one call issues (mirrors the
-    kernels' loop structure)."""
-    L = 64
-    nc = math.ceil(w.T / L)
+    """v_mfma_f32_16x16x32_bf16 instructions one call issues on the fast path
+    (mirrors the kernels' loop structure: per chunk and wave, the score tiles
+    up to the wave's own block, the score x value products, the product with
+    the carried state, and the state update)."""
+    sp, sv = (2, 1) if w.dtype == "bf16" else (3, 3)
+
+    def prods(sa, sb):
+        m = max(sa, sb)
+        return sum(1 for d in range(m) for i in range(d + 1) if i < sa and d - i < sb)
+
+    def sweep(n, out, have_s):
+        nch, tot = math.ceil(n / 64), 0
+        for ch in range(nch):
+            lv = min(64, n - 64 * ch)
+            if out:
+                for J in range(4):
+                    if 16 * J >= lv:
+                        continue
+                    tot += (J + 1) * 2 * prods(sp, sp)
+                    tot += (J // 2 + 1) * 4 * prods(sv, sp)
+                    if ch > 0 or have_s:
+                        tot += 2 * 4 * prods(sp, sp)
+            if not (out and ch == nch - 1):
+                tot += 4 * (2 if lv > 32 else 1) * 4 * prods(sp, sv)
+        return tot
+
+    g, segc = plan_segments(w)
     bidir = w.mode == "bidirectional"
-    vsplit = 3 if w.dtype == "f32" else 2   # products with the value tile
     per_bh = 0
-    for ch in range(nc):
-        lv = min(L, w.T - ch * L)
-        for wave in range(4):
-            if 16 * wave >= lv:
-                continue
-            tiles = (wave + 1) + ((4 - wave) if bidir else 0)
-            per_bh += tiles * 2 * 3                                  # in-chunk scores
-            ksteps = 2 if bidir else (1 if wave < 2 else 2)
-            per_bh += ksteps * 4 * vsplit                            # scores x V
-            if ch > 0:
-                per_bh += 2 * 4 * 3                                  # left state
-            if bidir and ch < nc - 1:
-                per_bh += 2 * 4 * 3                                  # right state
-        if ch < nc - 1:
-            per_bh += 4 * 2 * 4 * vsplit                             # state update
-        if bidir and ch >= 1:
-            per_bh += 4 * 2 * 4 * vsplit                             # reverse sweep
+    for seg in range(g):
+        n = min(w.T, (seg + 1) * segc * 64) - seg * segc * 64
+        per_bh += sweep(n, True, seg > 0)
+        if bidir:
+            per_bh += sweep(n, True, seg < g - 1)
+        if g > 1:
+            if seg < g - 1:
+                per_bh += sweep(n, False, False)
+            if bidir and seg > 0:
+                per_bh += sweep(n, False, False)
     return per_bh * w.B * w.H
 
 
@@ -230,7 +271,8 @@ def main() -> int:
                    "rotating_copies": ncopy, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "wkv6 forward call (reverse-state + forward kernels)",
+                     "kernel": "wkv6_fwd call: fast-path sweep kernel + fix-up kernel"
+                               + (" + segment summary kernels" if plan_segments(w)[0] > 1 else ""),
                      "mean_call_ms": mean_ms, "algorithmic_bytes": alg_bytes},
         "mfma": {"instructions": n_mfma, "executed_tflops": mfma_tflops,
                  "util": mfma_tflops / MFMA_BF16_PEAK_TFLOPS, "peak_tflops": MFMA_BF16_PEAK_TFLOPS},

@@ -78,9 +78,15 @@ extern "C" {
  *   stream        a hipStream_t passed as void* (NULL = the null stream).
  *
  * Ownership: every pointer is caller-owned device memory; the library keeps
- * none of them after returning.  Bidirectional calls with T > 64 take a
- * temporary device workspace of B*H*(ceil(T/64)-1)*16 KiB, allocated and
- * released in stream order (hipMallocAsync / hipFreeAsync on `stream`).
+ * none of them after returning.  When B*H is small the library cuts each
+ * sequence into segments handled by different workgroups (more when the
+ * sequences are long enough); such calls take a temporary device workspace
+ * of B*H*segments*2*(64*64+64)*4 bytes for the segment summaries, allocated
+ * and released in stream order (hipMallocAsync / hipFreeAsync on `stream`).
+ * Other calls allocate nothing.  y is written in place while the call runs:
+ * a bidirectional call first stores the later-token part of every row and
+ * then adds the rest, so y must not be read before the stream has run the
+ * call.
  *
  * Execution: asynchronous on `stream`; the call does not synchronise the
  * host.  The caller keeps the buffers alive until the stream has run the

@@ -8,42 +8,45 @@
 // Implementation in kernel_forward"; "RWKV Architecture" page, sections
 // "RWKV-5 Eagle" and "RWKV-6 Finch".)
 //
-// Chunked form.  Tokens are processed in chunks of L = 64.  With lambda = log2
-// of the decay (computed directly as -log2(e) exp(w_raw), never as the log of
-// a rounded w) and Lin / Lex its inclusive / exclusive prefix sums over the
-// chunk, every decay product the definition needs is a power of two of a
-// difference of prefix sums (the log-space prefix-scan view of the "RWKV
-// Architecture" page, section "The Parallel Training Formulation"):
-//   past token i < t of the chunk:   2^(Lex_t - Lin_i)
-//   later token i > t of the chunk:  2^(Lex_i - Lin_t)
-//   state entering from the left:    2^(Lex_t)           (scales r_t)
-//   state entering from the right:   2^(Ltot - Lin_t)
-//   state leaving to the right:      2^Ltot S + sum_i (k_i 2^(Ltot - Lin_i))^T v_i
-//   state leaving to the left:       2^Ltot S + sum_i (k_i 2^(Lex_i))^T v_i
+// Sweeps.  The later-token sum of the bidirectional mode is the causal sum of
+// the reversed sequence without the u term, so one sweep routine serves both
+// directions: the reverse sweep runs over the tokens from the last one down
+// and writes y, then the forward sweep adds its part (same workgroup, so the
+// partial rows come back from the XCD's L2).  A causal call is the forward
+// sweep alone.
 //
-// Fast path (chunk span |Ltot| < 96 for every channel): the in-chunk decay
-// splits at the chunk start, keys k 2^(-Lin) and queries r 2^(Lex) (and
-// k 2^(Lex - Ltot), r 2^(Ltot - Lin) for later tokens), so one query operand
-// serves both the in-chunk scores and the state product, and the state update
-// becomes 2^Ltot (S + (k 2^(-Lin))^T V) with the row scale applied to the fp32
-// accumulator.  Two exponentials per element.
-// Slow path (some channel decays by more than 2^-96 over the chunk): the
-// score tile of key block I (16 tokens) splits at that block's boundary,
-// 2^(Lex_t - E_I) 2^(E_I - Lin_i) for i < t with E_I the prefix at the end of
-// block I, and 2^(B_I - Lin_t) 2^(Lex_i - B_I) for i > t with B_I the prefix
-// before block I.  Off the diagonal both factors are <= 1 and each is >= the
-// true weight, so a factor only underflows where the weight is below 2^-126;
-// on the diagonal they stay within 2^(+-15 |lambda|).  Valid for w_raw <= 1.5.
-// The choice is made per chunk, uniformly for the workgroup.
+// Chunked form.  A sweep takes its tokens in chunks of L = 64 (in sweep order;
+// only the last chunk may be short).  With lambda = log2 of the decay
+// (computed directly as -log2(e) exp(w_raw), never as the log of a rounded w)
+// and Lin / Lex its inclusive / exclusive prefix sums over the chunk, every
+// decay product the definition needs is a power of two of a difference of
+// prefix sums (the log-space prefix-scan view of the "RWKV Architecture" page,
+// section "The Parallel Training Formulation"):
+//   earlier token i < t of the chunk:  2^(Lex_t - Lin_i)
+//   state entering the chunk:          2^(Lex_t)            (scales r_t)
+//   state leaving the chunk:           2^Ltot S + sum_i (k_i 2^(Ltot - Lin_i))^T v_i
+//
+// Fast path (every 16-token block of the chunk decays by less than 2^-24 in
+// every channel, so the chunk by less than 2^-96): the in-chunk decay splits
+// at the chunk start, keys k 2^(-Lin) and queries r 2^(Lex), so one query
+// operand serves both the in-chunk scores and the state product, and the
+// state update becomes 2^Ltot (S + (k 2^(-Lin))^T V) with the row scale
+// applied to the fp32 accumulator.  Two exponentials per element.
+// Slow path (some channel decays faster): the score tile of key block I
+// splits at that block's end, 2^(Lex_t - E_I) 2^(E_I - Lin_i) with E_I the
+// prefix at the end of block I; off the diagonal both factors are <= 1 and
+// each is >= the true weight, so a factor only underflows where the weight is
+// below 2^-126, and on the diagonal they stay within 2^(+-15 |lambda|).
+// Valid for w_raw <= 1.5.  The fast kernels give up on an item at its first
+// slow chunk and a fix-up kernel recomputes that item with the general
+// sweeps (see the kernels at the end of this file).
 //
 // Segments.  When few (batch, head) pairs exist, each sequence is cut into G
-// segments of whole chunks handled by different workgroups.  seg_kernel
-// sweeps each segment from its last chunk to its first and writes (a) the
-// state each chunk receives from the later chunks of its own segment
-// (bidirectional mode) and (b) per segment the forward end state F, the
-// backward start state R and the total log2 decay g (G > 1).  fwd_kernel
-// combines the other segments' summaries with the associative rule
-// (g1, S1) o (g2, S2) = (g1 + g2, 2^g2 S1 + S2) and sweeps its segment.
+// segments of whole chunks handled by different workgroups.  A summary pass
+// sweeps each segment from a zero state and stores its end state and total
+// log2 decay g per direction; each segment's sweep then starts from the
+// combination of the earlier segments' summaries (in sweep order) under the
+// associative rule (g1, S1) o (g2, S2) = (g1 + g2, 2^g2 S1 + S2).
 //
 // Precision.  Every contraction runs on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation.  An fp32 operand x is carried as SP bf16 parts (x = p0 + p1
@@ -67,7 +70,8 @@
 // 16-lane row) and the query operands never touch LDS.  Wave J also owns
 // state rows 16J..16J+15 (all 64 value columns); the state is exchanged
 // through LDS once per chunk, pre-split.  LDS tiles are 64x64 bf16 planes
-// whose 16-byte chunks are XOR-swizzled by row.
+// whose 16-byte chunks are XOR-swizzled by row; a workgroup holds 41 KB of
+// LDS (bf16 inputs), so three fit on a CU.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
