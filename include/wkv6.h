@@ -54,8 +54,9 @@ extern "C" {
 #define WKV6_OK               0  /* success; also B == 0 or T == 0 (nothing done) */
 #define WKV6_ERR_INVALID_ARG  1  /* negative size, H < 1, C % H != 0, null pointer,
                                     unknown mode/dtype, y overlapping an input */
-#define WKV6_ERR_UNSUPPORTED  2  /* head size C / H other than 64, or a size whose
-                                    index arithmetic would overflow */
+#define WKV6_ERR_UNSUPPORTED  2  /* head size C / H other than 64, or sizes whose
+                                    index arithmetic would overflow (the kernels
+                                    need T * C * 4 < 2^31 - 4096) */
 #define WKV6_ERR_MISALIGNED   3  /* a pointer not aligned to 16 bytes */
 #define WKV6_ERR_HIP          4  /* a HIP runtime error (launch, allocation) */
 

@@ -57,7 +57,9 @@ int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const vo
     return fail(WKV6_ERR_INVALID_ARG, "unknown dtype");
   if (C / H != wkv6::kHead) return fail(WKV6_ERR_UNSUPPORTED, "head size C/H must be 64");
   if (B == 0 || T == 0) return WKV6_OK;
-  if (T > INT_MAX - wkv6::kChunk || B * H > INT_MAX || B > INT64_MAX / T || B * T > INT64_MAX / (4 * C))
+  // the kernels address one (batch, head) slice with 32-bit byte offsets
+  if (T > INT_MAX - wkv6::kChunk || B * H > INT_MAX || B > INT64_MAX / T || B * T > INT64_MAX / (4 * C) ||
+      T > (INT_MAX - 4096) / (4 * C))
     return fail(WKV6_ERR_UNSUPPORTED, "sizes exceed the supported index range");
   const void* ptrs[6] = {r, k, v, w_raw, u, y};
   const char* names[6] = {"r", "k", "v", "w_raw", "u", "y"};

@@ -289,19 +289,48 @@ struct Raw {
   uint4 q[BF16 ? 2 : 4];
 };
 
+// Global tensors are read and written through buffer descriptors whose base
+// is the (batch, head) slice: the base lives in scalar registers, a lane needs
+// one 32-bit byte offset, and an offset past the slice's last row reads zero
+// and drops a store (used for lanes past the sequence end).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcFlags = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
+constexpr int kOffNone = 0x7FFFFFF0;     // a byte offset past every slice
+
+__device__ __forceinline__ Rsrc slice_rsrc(const void* p, int64_t elem_off, int isz, int64_t T, int64_t C) {
+  char* base = const_cast<char*>(static_cast<const char*>(p)) + elem_off * isz;
+  const int nbytes = (int)(((T - 1) * C + HS) * isz);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, nbytes, kRsrcFlags);
+}
+
+__device__ __forceinline__ uint4 bload16(Rsrc r, int off) {
+  const auto q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(q[0], q[1], q[2], q[3]);
+}
+
+__device__ __forceinline__ float4 bloadf4(Rsrc r, int off) {
+  const auto q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_float4(__uint_as_float(q[0]), __uint_as_float(q[1]), __uint_as_float(q[2]), __uint_as_float(q[3]));
+}
+
+__device__ __forceinline__ void bstoref4(Rsrc r, int off, float a, float b, float c, float d) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 q = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+  __builtin_amdgcn_raw_buffer_store_b128(q, r, off, 0, 0);
+}
+
+// The lane's row: row_off is the row's byte offset in the slice.
 template <bool BF16>
-__device__ __forceinline__ Raw<BF16> gload(const void* base, int64_t row_off, int g) {
+__device__ __forceinline__ Raw<BF16> gload(Rsrc rs, int row_off, int g) {
   Raw<BF16> r;
   if constexpr (BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + row_off;
-    r.q[0] = *reinterpret_cast<const uint4*>(p + 8 * g);
-    r.q[1] = *reinterpret_cast<const uint4*>(p + 32 + 8 * g);
+    r.q[0] = bload16(rs, row_off + 16 * g);
+    r.q[1] = bload16(rs, row_off + 64 + 16 * g);
   } else {
-    const float* p = static_cast<const float*>(base) + row_off;
-    r.q[0] = *reinterpret_cast<const uint4*>(p + 8 * g);
-    r.q[1] = *reinterpret_cast<const uint4*>(p + 8 * g + 4);
-    r.q[2] = *reinterpret_cast<const uint4*>(p + 32 + 8 * g);
-    r.q[3] = *reinterpret_cast<const uint4*>(p + 32 + 8 * g + 4);
+    r.q[0] = bload16(rs, row_off + 32 * g);
+    r.q[1] = bload16(rs, row_off + 32 * g + 16);
+    r.q[2] = bload16(rs, row_off + 128 + 32 * g);
+    r.q[3] = bload16(rs, row_off + 128 + 32 * g + 16);
   }
   return r;
 }
@@ -536,7 +565,7 @@ __device__ __forceinline__ void write_vT(__bf16* sV, const int (&c)[8], const Ra
 // product are built in phase C from the raw r and w words.
 template <bool BF16, int MODE, bool DIAG>
 __device__ __forceinline__ void slow_chunk(const Params& p, char* lds, Raw<BF16> rraw, Raw<BF16> kraw,
-                                                     Raw<BF16> wraw, int64_t yoff, int Lv, bool left) {
+                                                     Raw<BF16> wraw, Rsrc ry, int yoff, int Lv, bool left) {
   constexpr int SP = BF16 ? 2 : 3;
   constexpr int SV = BF16 ? 1 : 3;
   constexpr bool OUT = MODE != kState;
@@ -649,19 +678,17 @@ __device__ __forceinline__ void slow_chunk(const Params& p, char* lds, Raw<BF16>
       for (int nt = 0; nt < 4; ++nt)
         Y[nt] = mma(rd4x2<SV>(sV, 1024 * nt + lo.v[pr][0], 1024 * nt + lo.v[pr][1]), mo, Y[nt]);
     }
-    if (valid) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        float4 o = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
-        if (MODE == kOutAcc) {
-          const float4 yo = *reinterpret_cast<const float4*>(p.y + yoff + 16 * nt + 4 * g);
-          o.x += yo.x;
-          o.y += yo.y;
-          o.z += yo.z;
-          o.w += yo.w;
-        }
-        *reinterpret_cast<float4*>(p.y + yoff + 16 * nt + 4 * g) = o;
+    for (int nt = 0; nt < 4; ++nt) {
+      float4 o = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
+      if (MODE == kOutAcc) {
+        const float4 yo = bloadf4(ry, yoff + 64 * nt);
+        o.x += yo.x;
+        o.y += yo.y;
+        o.z += yo.z;
+        o.w += yo.w;
       }
+      bstoref4(ry, yoff + 64 * nt, o.x, o.y, o.z, o.w);
     }
   }
 }
@@ -746,14 +773,19 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
   // The next chunk's loads are issued after the current chunk's outputs (the
   // other resident workgroups cover their latency); rows are clamped into the
   // segment so the loads are unconditional.
+  constexpr int ISZ = BF16 ? 2 : 4;
+  const Rsrc rr = slice_rsrc(p.r, base, ISZ, T, C), rk = slice_rsrc(p.k, base, ISZ, T, C);
+  const Rsrc rv = slice_rsrc(p.v, base, ISZ, T, C), rw = slice_rsrc(p.w, base, ISZ, T, C);
+  const Rsrc ry = slice_rsrc(p.y, base, 4, T, C);
   Raw<BF16> buf[4];
   auto fetch = [&](int ch) {
-    const int64_t q = min((int64_t)ch * LC + tau, n - 1);
-    const int64_t off = base + token(q) * C;
-    if (OUT) buf[0] = gload<BF16>(p.r, off, g);
-    buf[1] = gload<BF16>(p.k, off, g);
-    buf[2] = gload<BF16>(p.v, off, g);
-    buf[3] = gload<BF16>(p.w, off, g);
+    // rows past the segment are masked by `valid` where it matters; rows
+    // outside the sequence read zero
+    const int off = (int)(token((int64_t)ch * LC + tau) * C) * ISZ;
+    if (OUT) buf[0] = gload<BF16>(rr, off, g);
+    buf[1] = gload<BF16>(rk, off, g);
+    buf[2] = gload<BF16>(rv, off, g);
+    buf[3] = gload<BF16>(rw, off, g);
   };
   fetch(0);
 
@@ -787,13 +819,16 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // rows of y the reverse sweep left (kOutAcc) or from zero.
     Op<SP> q[2];
     float dg = 0.f;
-    const int64_t yoff = base + token((int64_t)ch * LC + tau) * C;
+    // byte offset of the lane's output row; lanes past the segment get an
+    // offset outside every slice, so their loads read zero and their stores
+    // are dropped without a branch
+    const int yoff = valid ? (int)(token((int64_t)ch * LC + tau) * C) * 4 + 16 * g : kOffNone;
     f32x4 Y[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (MODE == kOutAcc && valid) {
-        const float4 yo = *reinterpret_cast<const float4*>(p.y + yoff + 16 * nt + 4 * g);
+      if (MODE == kOutAcc) {
+        const float4 yo = bloadf4(ry, yoff + 64 * nt);
         Y[nt] = f32x4{yo.x, yo.y, yo.z, yo.w};
       }
     }
@@ -861,11 +896,8 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) Y[nt] = mma(rd8<SP>(sS, 1024 * nt + lo.a[ks]), q[ks], Y[nt]);
       }
-      if (valid) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          *reinterpret_cast<float4*>(p.y + yoff + 16 * nt + 4 * g) = make_float4(Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
-      }
+      for (int nt = 0; nt < 4; ++nt) bstoref4(ry, yoff + 64 * nt, Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
     }
     if (ch == nch - 1) {
       if (OUT) {
@@ -933,7 +965,9 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
       }
       lds_barrier();
 
-      slow_chunk<BF16, MODE, DIAG>(p, lds, buf[0], buf[1], buf[3], base + token((int64_t)ch * LC + tau) * C, Lv, left);
+      slow_chunk<BF16, MODE, DIAG>(p, lds, buf[0], buf[1], buf[3], ry,
+                                   valid ? (int)(token((int64_t)ch * LC + tau) * C) * 4 + 16 * g : kOffNone, Lv,
+                                   left);
       if (ch == nch - 1) {
         if (OUT) break;
       } else {

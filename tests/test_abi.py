@@ -49,6 +49,7 @@ def _call(B=2, T=8, C=128, H=2, ptrs=None, mode=0, dtype=0):
     (dict(C=96, H=2), wkv6.ERR_UNSUPPORTED),      # head size 48
     (dict(C=256, H=2), wkv6.ERR_UNSUPPORTED),     # head size 128
     (dict(T=2 ** 31), wkv6.ERR_UNSUPPORTED),
+    (dict(T=2 ** 20, C=512, H=8), wkv6.ERR_UNSUPPORTED),   # one slice beyond 2 GiB of fp32 rows
 ])
 def test_rejects_bad_arguments(kw, status):
     assert _call(**kw) == status
