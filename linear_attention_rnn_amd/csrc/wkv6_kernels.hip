@@ -815,8 +815,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     if (chunk_is_slow(sFlag)) break;   // uniform: every wave reads the same flags
 
     // ---- phase B (fast): keys k 2^(-Lin) to LDS; queries r 2^Lex split in
-    // registers; bonus diagonal.  The output accumulators start from the
-    // rows of y the reverse sweep left (kOutAcc) or from zero.
+    // registers; bonus diagonal.
     Op<SP> q[2];
     float dg = 0.f;
     // byte offset of the lane's output row; lanes past the segment get an
@@ -824,14 +823,6 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // are dropped without a branch
     const int yoff = valid ? (int)(token((int64_t)ch * LC + tau) * C) * 4 + 16 * g : kOffNone;
     f32x4 Y[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (MODE == kOutAcc) {
-        const float4 yo = bloadf4(ry, yoff + 64 * nt);
-        Y[nt] = f32x4{yo.x, yo.y, yo.z, yo.w};
-      }
-    }
     if (active) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -861,6 +852,16 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // ---- phase C (fast): scores of the key blocks up to the lane's own,
     // outputs
     if (OUT && active) {
+      // the output accumulators start from the rows of y the reverse sweep
+      // left (kOutAcc) or from zero
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (MODE == kOutAcc) {
+          const float4 yo = bloadf4(ry, yoff + 64 * nt);
+          Y[nt] = f32x4{yo.x, yo.y, yo.z, yo.w};
+        }
+      }
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         const int I0 = 2 * pr;
