@@ -157,15 +157,24 @@ struct Op {
 
 template <int S>
 __device__ __forceinline__ Op<S> split8(const float* x) {
+  // Pairs are rounded together (one packed conversion per pair and part);
+  // the parts are read back from the packed bits to form the remainders.
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   Op<S> o;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float r = x[j];
+  for (int jp = 0; jp < 4; ++jp) {
+    float r0 = x[2 * jp], r1 = x[2 * jp + 1];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const __bf16 h = (__bf16)r;
-      o.p[s][j] = h;
-      r -= (float)h;
+      const bf16x2 h = __builtin_convertvector(f32x2{r0, r1}, bf16x2);
+      o.p[s][2 * jp] = h[0];
+      o.p[s][2 * jp + 1] = h[1];
+      if (s + 1 < S) {
+        const uint32_t bits = __builtin_bit_cast(uint32_t, h);
+        r0 -= __uint_as_float(bits << 16);
+        r1 -= __uint_as_float(bits & 0xFFFF0000u);
+      }
     }
   }
   return o;
@@ -259,15 +268,22 @@ __device__ __forceinline__ void wr8(__bf16* P, int off, const float* x) {
 
 template <int S>
 __device__ __forceinline__ void wr4(__bf16* P, int off, const float* x) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   float r[4] = {x[0], x[1], x[2], x[3]};
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     bf16x4 q;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const __bf16 h = (__bf16)r[j];
-      q[j] = h;
-      r[j] -= (float)h;
+    for (int jp = 0; jp < 2; ++jp) {
+      const bf16x2 h = __builtin_convertvector(f32x2{r[2 * jp], r[2 * jp + 1]}, bf16x2);
+      q[2 * jp] = h[0];
+      q[2 * jp + 1] = h[1];
+      if (s + 1 < S) {
+        const uint32_t bits = __builtin_bit_cast(uint32_t, h);
+        r[2 * jp] -= __uint_as_float(bits << 16);
+        r[2 * jp + 1] -= __uint_as_float(bits & 0xFFFF0000u);
+      }
     }
     *reinterpret_cast<bf16x4*>(P + s * PL + off) = q;
   }
