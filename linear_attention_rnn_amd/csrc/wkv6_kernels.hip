@@ -132,9 +132,6 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, f32x4 c)
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// log2 of the decay: log2(exp(-exp(w_raw))) = -log2(e) exp(w_raw).
-__device__ __forceinline__ float log2_decay(float w_raw) { return -kLog2e * ex2(w_raw * kLog2e); }
-
 // Workgroup barrier for LDS hand-offs only.  Waves of a workgroup exchange
 // data through LDS alone, so the barrier waits for this wave's LDS operations
 // (lgkmcnt) but leaves global loads (the next chunk's prefetch) and global
@@ -155,26 +152,47 @@ struct Op {
   bf16x8 p[S];
 };
 
-template <int S>
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// A pair rounded to bf16 by one packed conversion.
+__device__ __forceinline__ bf16x2 round_pair(float a, float b) {
+  return __builtin_convertvector(f32x2{a, b}, bf16x2);
+}
+
+// r0 -= h[0], r1 -= h[1] for h = round_pair(r0, r1); the differences are
+// exactly representable.  DOT: one bf16 dot product per element, with the
+// operand (-1, 0) or (0, -1), accumulating in place (for operands that die
+// here); else the rounded parts are unpacked and subtracted.  (-1, 0) is
+// loaded into a scalar register by hand: written as a constant the compiler
+// encodes it as the inline constant -1.0, which the dot product reads as the
+// 32-bit pattern of -1.0f, i.e. the pair (0, -1).
+template <bool DOT>
+__device__ __forceinline__ void drop_rounded(bf16x2 h, float& r0, float& r1) {
+  if constexpr (DOT) {
+    uint32_t neg_lo;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(neg_lo));
+    r0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg_lo), r0, false);
+    r1 = __builtin_amdgcn_fdot2_f32_bf16(h, bf16x2{(__bf16)0.f, (__bf16)-1.f}, r1, false);
+  } else {
+    const uint32_t bits = __builtin_bit_cast(uint32_t, h);
+    r0 -= __uint_as_float(bits << 16);
+    r1 -= __uint_as_float(bits & 0xFFFF0000u);
+  }
+}
+
+template <int S, bool DOT = true>
 __device__ __forceinline__ Op<S> split8(const float* x) {
-  // Pairs are rounded together (one packed conversion per pair and part);
-  // the parts are read back from the packed bits to form the remainders.
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   Op<S> o;
 #pragma unroll
   for (int jp = 0; jp < 4; ++jp) {
     float r0 = x[2 * jp], r1 = x[2 * jp + 1];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const bf16x2 h = __builtin_convertvector(f32x2{r0, r1}, bf16x2);
+      const bf16x2 h = round_pair(r0, r1);
       o.p[s][2 * jp] = h[0];
       o.p[s][2 * jp + 1] = h[1];
-      if (s + 1 < S) {
-        const uint32_t bits = __builtin_bit_cast(uint32_t, h);
-        r0 -= __uint_as_float(bits << 16);
-        r1 -= __uint_as_float(bits & 0xFFFF0000u);
-      }
+      if (s + 1 < S) drop_rounded<DOT>(h, r0, r1);
     }
   }
   return o;
@@ -205,11 +223,14 @@ __device__ __forceinline__ int swz(int row, int col) {
 //   a[ks]     row li, 16-byte chunk 4 ks + g          (+1024 per 16 rows)
 //   v[pr][h]  row li, 8 bytes at column 16 (2 pr + h) + 4 g
 //   c[j]      row 8 g + j, column tau                  (+2048 per 32 rows)
+//   kt[h]     row 8 g + li / 4 + 4 h, 8 bytes at column 16 J + 4 (li % 4)
+//             (transposed reads, +2048 per 32 rows)
 //   s         row li, 8 bytes at column 16 J + 4 g
 struct LdsOff {
   int a[2];
   int v[2][2];
   int c[8];
+  int kt[2];
   int s;
 };
 
@@ -224,6 +245,11 @@ __device__ __forceinline__ LdsOff lds_offsets(int J, int g, int li) {
     for (int h = 0; h < 2; ++h) o.v[pr][h] = li * 64 + (((4 * pr + 2 * h + (g >> 1)) ^ x) << 3) + 4 * (g & 1);
 #pragma unroll
   for (int j = 0; j < 8; ++j) o.c[j] = (8 * g + j) * 64 + ((((tau >> 3)) ^ j) << 3) + (tau & 7);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int m = (li >> 2) + 4 * h, q = li & 3;
+    o.kt[h] = (8 * g + m) * 64 + (((2 * J + (q >> 1)) ^ m) << 3) + 4 * (q & 1);
+  }
   o.s = li * 64 + (((2 * J + (g >> 1)) ^ x) << 3) + 4 * (g & 1);
   return o;
 }
@@ -248,14 +274,27 @@ __device__ __forceinline__ Op<S> rd4x2(const __bf16* P, int o0, int o1) {
   return o;
 }
 
-// k-slot j from offset add + c[j] (a column read down 8 stored rows)
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// 4m + n supplies the address of 4 consecutive bf16 values; lane i of the
+// group receives element i % 4 of the values addressed by lanes 4m + i / 4,
+// m = 0..3, in the order of m.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 ld_tr(const __bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
+
+// A column of a plane as an MFMA A operand: lane (g, i) gets k-slots
+// 8g..8g+7 = rows 8g..8g+7 of column 16 J + i (offsets kt, plus add).
 template <int S>
-__device__ __forceinline__ Op<S> rdcol8(const __bf16* P, const int (&c)[8], int add) {
+__device__ __forceinline__ Op<S> rdcol8(const __bf16* P, const int (&kt)[2], int add) {
   Op<S> o;
 #pragma unroll
-  for (int s = 0; s < S; ++s)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o.p[s][j] = P[s * PL + add + c[j]];
+  for (int s = 0; s < S; ++s) {
+    const bf16x4 a = ld_tr(P + s * PL + add + kt[0]);
+    const bf16x4 b = ld_tr(P + s * PL + add + kt[1]);
+    o.p[s] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
   return o;
 }
 
@@ -268,22 +307,16 @@ __device__ __forceinline__ void wr8(__bf16* P, int off, const float* x) {
 
 template <int S>
 __device__ __forceinline__ void wr4(__bf16* P, int off, const float* x) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   float r[4] = {x[0], x[1], x[2], x[3]};
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     bf16x4 q;
 #pragma unroll
     for (int jp = 0; jp < 2; ++jp) {
-      const bf16x2 h = __builtin_convertvector(f32x2{r[2 * jp], r[2 * jp + 1]}, bf16x2);
+      const bf16x2 h = round_pair(r[2 * jp], r[2 * jp + 1]);
       q[2 * jp] = h[0];
       q[2 * jp + 1] = h[1];
-      if (s + 1 < S) {
-        const uint32_t bits = __builtin_bit_cast(uint32_t, h);
-        r[2 * jp] -= __uint_as_float(bits << 16);
-        r[2 * jp + 1] -= __uint_as_float(bits & 0xFFFF0000u);
-      }
+      if (s + 1 < S) drop_rounded<false>(h, r[2 * jp], r[2 * jp + 1]);
     }
     *reinterpret_cast<bf16x4*>(P + s * PL + off) = q;
   }
@@ -308,10 +341,13 @@ struct Raw {
 // Global tensors are read and written through buffer descriptors whose base
 // is the (batch, head) slice: the base lives in scalar registers, a lane needs
 // one 32-bit byte offset, and an offset past the slice's last row reads zero
-// and drops a store (used for lanes past the sequence end).
+// and drops a store.  Lanes whose token lies past the segment use such an
+// offset, so their keys, values and queries are zero without any masking.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcFlags = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
-constexpr int kOffNone = 0x7FFFFFF0;     // a byte offset past every slice
+// A byte offset past every slice (slices stay below 2^31 - 4096 bytes), small
+// enough that adding a row's in-row offset does not overflow.
+constexpr int kOffNone = 0x7FFFF000;
 
 __device__ __forceinline__ Rsrc slice_rsrc(const void* p, int64_t elem_off, int isz, int64_t T, int64_t C) {
   char* base = const_cast<char*>(static_cast<const char*>(p)) + elem_off * isz;
@@ -382,20 +418,21 @@ __device__ __forceinline__ void load8f(const float* p, float (&o)[8]) {
 // ---- prefix sums of the chunk for the lane's 16 home elements
 //
 // block_scan: lambda and its inclusive prefix inside the lane's 16-token block
-// (DPP row shifts within each 16-lane row; lanes past the sequence end
-// contribute lambda = 0).  Lane 15 of each row then holds the block totals,
+// (DPP row shifts within each 16-lane row).  nl is -log2(e) for a token of the
+// segment and 0 past it, so such tokens contribute lambda = 0 (their w_raw
+// reads as 0).  Lane 15 of each row then holds the block totals,
 // which go to sBT[J][c].  Block offsets and chunk totals are summed from sBT
 // in block order everywhere, so an exclusive prefix and the preceding
 // inclusive prefix are bit-identical.
 template <bool BF16>
-__device__ __forceinline__ void block_scan(const Raw<BF16>& rw, bool valid, float (&lin)[2][8]) {
+__device__ __forceinline__ void block_scan(const Raw<BF16>& rw, float nl, float (&lin)[2][8]) {
   float w[2][8];
   unpack<BF16>(rw, w);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float x = valid ? log2_decay(w[ks][j]) : 0.f;
+      float x = nl * ex2(w[ks][j] * kLog2e);
       x += row_shr<1>(x);
       x += row_shr<2>(x);
       x += row_shr<4>(x);
@@ -408,12 +445,12 @@ __device__ __forceinline__ void block_scan(const Raw<BF16>& rw, bool valid, floa
 // decays by 2^-kBlockSpan or more (then the chunk takes the slow path).
 __device__ __forceinline__ void publish_block(const float (&lin)[2][8], float* sBT, int* sFlag, int J, int g,
                                               int li, int lane) {
-  bool big = false;
+  float mn = lin[0][0];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) big |= lin[ks][j] < -kBlockSpan;
-  big = __any(li == 15 && big);
+    for (int j = 0; j < 8; ++j) mn = fminf(mn, lin[ks][j]);
+  const bool big = __any(li == 15 && mn < -kBlockSpan);
   if (li == 15) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -439,10 +476,14 @@ __device__ __forceinline__ bool chunk_is_slow(const int* sFlag) {
 // Sum of the block totals before block J (the block's offset) for 8
 // consecutive channels.
 __device__ __forceinline__ void block_offset(const float* sBT, int J, int cb, float (&off)[8]) {
+  if (J == 0) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) off[j] = 0.f;
+    for (int j = 0; j < 8; ++j) off[j] = 0.f;
+    return;
+  }
+  load8f(&sBT[cb], off);
 #pragma unroll
-  for (int I = 0; I < 3; ++I) {
+  for (int I = 1; I < 3; ++I) {
     if (I < J) {
       float b[8];
       load8f(&sBT[I * 64 + cb], b);
@@ -539,25 +580,15 @@ __device__ __forceinline__ void unpack_half(const Raw<BF16>& r, int ks, float (&
   }
 }
 
-// Half ks of a raw row as floats, zero for a token past the sequence end
-// (the loads read a clamped, valid row; its values must not leak into keys).
-template <bool BF16>
-__device__ __forceinline__ void unpack_half_masked(const Raw<BF16>& r, int ks, bool valid, float (&o)[8]) {
-  unpack_half<BF16>(r, ks, o);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = valid ? o[j] : 0.f;
-}
-
 // V^T columns of the lane's token: element (32 ks + 8 g + j, tau) for its 16
-// home channels; zero for a token past the sequence end.  bf16 values are
-// stored as they were read.
+// home channels.  bf16 values are stored as they were read.
 template <bool BF16>
-__device__ __forceinline__ void write_vT(__bf16* sV, const int (&c)[8], const Raw<BF16>& r, bool valid) {
+__device__ __forceinline__ void write_vT(__bf16* sV, const int (&c)[8], const Raw<BF16>& r) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     if constexpr (BF16) {
       const uint4 q = r.q[ks];
-      const uint32_t w4[4] = {valid ? q.x : 0u, valid ? q.y : 0u, valid ? q.z : 0u, valid ? q.w : 0u};
+      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         sV[2048 * ks + c[2 * j]] = __builtin_bit_cast(__bf16, (unsigned short)(w4[j] & 0xFFFFu));
@@ -565,7 +596,7 @@ __device__ __forceinline__ void write_vT(__bf16* sV, const int (&c)[8], const Ra
       }
     } else {
       float v[8];
-      unpack_half_masked<BF16>(r, ks, valid, v);
+      unpack_half<BF16>(r, ks, v);
 #pragma unroll
       for (int j = 0; j < 8; ++j) wr1<3>(sV, 2048 * ks + c[j], v[j]);
     }
@@ -597,10 +628,10 @@ __device__ __forceinline__ void slow_chunk(const Params& p, char* lds, Raw<BF16>
   const int g = lane >> 4, li = lane & 15;
   const int tau = 16 * J + li;
   const LdsOff lo = lds_offsets(J, g, li);
-  const bool valid = tau < Lv;
+  const float nl = tau < Lv ? -kLog2e : 0.f;
   const bool active = 16 * J < Lv;
   float lin[2][8];
-  if (active) block_scan<BF16>(wraw, valid, lin);
+  if (active) block_scan<BF16>(wraw, nl, lin);
 
   // ---- phase B (slow)
   float dg = 0.f;
@@ -610,7 +641,7 @@ __device__ __forceinline__ void slow_chunk(const Params& p, char* lds, Raw<BF16>
       const int cb = 32 * ks + 8 * g;
       float off[8], k[8], kf[8];
       block_offset(sBT, J, cb, off);
-      unpack_half_masked<BF16>(kraw, ks, valid, k);
+      unpack_half<BF16>(kraw, ks, k);
       float r[8], uu[8];
       if (DIAG) {
         unpack_half<BF16>(rraw, ks, r);
@@ -635,7 +666,7 @@ __device__ __forceinline__ void slow_chunk(const Params& p, char* lds, Raw<BF16>
   if (OUT && active) {
     // Lin and Lex of the lane's elements, rebuilt from the raw w words
     float lns[2][8], lxs[2][8];
-    block_scan<BF16>(wraw, valid, lns);
+    block_scan<BF16>(wraw, nl, lns);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float off[8];
@@ -747,7 +778,12 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
   const int64_t t_hi = min(T, t_lo + (int64_t)p.SEGC * LC);
   const int64_t n = t_hi - t_lo;
   const int nch = (int)((n + LC - 1) / LC);
-  auto token = [&](int64_t q) { return REV ? t_hi - 1 - q : t_lo + q; };
+  // Sweep position q is token t_lo + q (REV: t_hi - 1 - q).  Byte offsets of
+  // the lane's rows in chunk ch are row0 + ch * step (32-bit: slices stay
+  // below 2^31 bytes).
+  const int dir_rows = REV ? -1 : 1;
+  const int tok0 = (int)(REV ? t_hi - 1 : t_lo) + dir_rows * tau;
+  const int Ci = (int)C;
 
   if (DIAG && tid < 64) sU[tid] = p.u[h * HS + tid];   // read after the first barrier
 
@@ -787,17 +823,18 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 
   // Raw rows of the lane's token for the chunk: [0] r, [1] k, [2] v, [3] w.
   // The next chunk's loads are issued after the current chunk's outputs (the
-  // other resident workgroups cover their latency); rows are clamped into the
-  // segment so the loads are unconditional.
+  // other resident workgroups cover their latency); the loads are
+  // unconditional, tokens past the segment reading zero.
   constexpr int ISZ = BF16 ? 2 : 4;
   const Rsrc rr = slice_rsrc(p.r, base, ISZ, T, C), rk = slice_rsrc(p.k, base, ISZ, T, C);
   const Rsrc rv = slice_rsrc(p.v, base, ISZ, T, C), rw = slice_rsrc(p.w, base, ISZ, T, C);
   const Rsrc ry = slice_rsrc(p.y, base, 4, T, C);
   Raw<BF16> buf[4];
+  const int in_row0 = tok0 * Ci * ISZ, in_step = dir_rows * LC * Ci * ISZ;
+  const int y_row0 = tok0 * Ci * 4 + 16 * g, y_step = dir_rows * LC * Ci * 4;
   auto fetch = [&](int ch) {
-    // rows past the segment are masked by `valid` where it matters; rows
-    // outside the sequence read zero
-    const int off = (int)(token((int64_t)ch * LC + tau) * C) * ISZ;
+    // tokens past the segment read zero
+    const int off = tau < (int)min<int64_t>(LC, n - (int64_t)ch * LC) ? in_row0 + ch * in_step : kOffNone;
     if (OUT) buf[0] = gload<BF16>(rr, off, g);
     buf[1] = gload<BF16>(rk, off, g);
     buf[2] = gload<BF16>(rv, off, g);
@@ -819,9 +856,9 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // ---- phase A: in-block scan, block totals, values
     float lin[2][8];
     if (active) {
-      block_scan<BF16>(buf[3], valid, lin);
+      block_scan<BF16>(buf[3], valid ? -kLog2e : 0.f, lin);
       publish_block(lin, sBT, sFlag, J, g, li, lane);
-      write_vT<BF16>(sV, lo.c, buf[2], valid);
+      write_vT<BF16>(sV, lo.c, buf[2]);
     } else {
       publish_empty_block(sBT, sFlag, J, lane);
       zero_cols16<SV>(sV, 16 * J, lane);
@@ -837,7 +874,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // byte offset of the lane's output row; lanes past the segment get an
     // offset outside every slice, so their loads read zero and their stores
     // are dropped without a branch
-    const int yoff = valid ? (int)(token((int64_t)ch * LC + tau) * C) * 4 + 16 * g : kOffNone;
+    const int yoff = valid ? y_row0 + ch * y_step : kOffNone;
     f32x4 Y[4];
     if (active) {
 #pragma unroll
@@ -845,7 +882,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
         const int cb = 32 * ks + 8 * g;
         float off[8], k[8], kf[8];
         block_offset(sBT, J, cb, off);
-        unpack_half_masked<BF16>(buf[1], ks, valid, k);
+        unpack_half<BF16>(buf[1], ks, k);
         float r[8], uu[8], qf[8];
         if (OUT) unpack_half<BF16>(buf[0], ks, r);
         if (DIAG) load8f(&sU[cb], uu);
@@ -891,14 +928,12 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) a = mma(rd8<SP>(sK, 1024 * I + lo.a[ks]), q[ks], a);
           }
+          // key i < tau keeps its score (every key of an earlier block
+          // does; a is zero for a later block), i == tau takes the bonus
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 16 * I + 4 * g + j;
-            float val;
-            if (I < J) val = a[j];
-            else if (I > J) val = 0.f;
-            else val = i < tau ? a[j] : ((DIAG && i == tau) ? dg : 0.f);
-            mx[4 * hh + j] = val;
+            mx[4 * hh + j] = i < tau ? a[j] : ((DIAG && i == tau) ? dg : 0.f);
           }
         }
         const Op<SP> mo = split8<SP>(mx);
@@ -940,7 +975,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if (32 * ks >= Lv) break;
-      const Op<SP> key = rdcol8<SP>(sK, lo.c, 2048 * ks);
+      const Op<SP> key = rdcol8<SP>(sK, lo.kt, 2048 * ks);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) S[nt] = mma(key, rd8<SV>(sV, 1024 * nt + lo.a[ks]), S[nt]);
     }
@@ -972,9 +1007,9 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
       // ---- phase A: in-block scan, block totals, values
       float lin[2][8];
       if (active) {
-        block_scan<BF16>(buf[3], valid, lin);
+        block_scan<BF16>(buf[3], valid ? -kLog2e : 0.f, lin);
         publish_block(lin, sBT, sFlag, J, g, li, lane);
-        write_vT<BF16>(sV, lo.c, buf[2], valid);
+        write_vT<BF16>(sV, lo.c, buf[2]);
       } else {
         publish_empty_block(sBT, sFlag, J, lane);
         zero_cols16<SV>(sV, 16 * J, lane);
@@ -983,7 +1018,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
       lds_barrier();
 
       slow_chunk<BF16, MODE, DIAG>(p, lds, buf[0], buf[1], buf[3], ry,
-                                   valid ? (int)(token((int64_t)ch * LC + tau) * C) * 4 + 16 * g : kOffNone, Lv,
+                                   valid ? y_row0 + ch * y_step : kOffNone, Lv,
                                    left);
       if (ch == nch - 1) {
         if (OUT) break;
@@ -1010,7 +1045,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
   #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if (32 * ks >= Lv) break;
-        Op<SP> key = rdcol8<SP>(sK, lo.c, 2048 * ks);
+        Op<SP> key = rdcol8<SP>(sK, lo.kt, 2048 * ks);
         // rows 32ks + 8g .. + 7 lie in token block I = 2ks + g / 2
         const int c = 16 * J + li;
         const int I = 2 * ks + (g >> 1);
