@@ -811,15 +811,19 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
       }
     }
     have_S = nprev > 0;
-    if (OUT && have_S) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
-        wr4<SP>(sS, 1024 * nt + lo.s, x);
-      }
-    }
   }
   float gsum[4] = {0.f, 0.f, 0.f, 0.f};   // kState: total log2 decay of the state rows
+
+  // The state entering a chunk goes to sS (pre-split) right after the chunk's
+  // first barrier: every wave has then finished the previous chunk's phase C,
+  // the last reader of sS, so phase D itself needs no barrier in front.
+  auto publish_state = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
+      wr4<SP>(sS, 1024 * nt + lo.s, x);
+    }
+  };
 
   // Raw rows of the lane's token for the chunk: [0] r, [1] k, [2] v, [3] w.
   // The next chunk's loads are issued after the current chunk's outputs (the
@@ -852,6 +856,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     const bool active = 16 * J < Lv;   // uniform in the wave
     const bool left = ch > 0 || have_S;
     lds_barrier();
+    if (OUT && left) publish_state();
 
     // ---- phase A: in-block scan, block totals, values
     float lin[2][8];
@@ -876,6 +881,18 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // are dropped without a branch
     const int yoff = valid ? y_row0 + ch * y_step : kOffNone;
     f32x4 Y[4];
+    if (OUT && active) {
+      // the output accumulators start from the rows of y the reverse sweep
+      // left (kOutAcc) or from zero; loaded here, a phase ahead of their use
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (MODE == kOutAcc) {
+          const float4 yo = bloadf4(ry, yoff + 64 * nt);
+          Y[nt] = f32x4{yo.x, yo.y, yo.z, yo.w};
+        }
+      }
+    }
     if (active) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -905,16 +922,6 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // ---- phase C (fast): scores of the key blocks up to the lane's own,
     // outputs
     if (OUT && active) {
-      // the output accumulators start from the rows of y the reverse sweep
-      // left (kOutAcc) or from zero
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (MODE == kOutAcc) {
-          const float4 yo = bloadf4(ry, yoff + 64 * nt);
-          Y[nt] = f32x4{yo.x, yo.y, yo.z, yo.w};
-        }
-      }
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         const int I0 = 2 * pr;
@@ -959,12 +966,11 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     } else {
       fetch(ch + 1);
     }
-    lds_barrier();   // every wave has finished reading sS
 
-    // ---- phase D: state rows 16J + 4g + j.  Keys are read down the columns
-    // of sK; fast: S <- 2^Ltot (S + K^T V) with keys k 2^(-Lin); slow: the
-    // keys of token block I are rescaled to k 2^(Ltot - Lin) and
-    // S <- 2^Ltot S + K^T V.
+    // ---- phase D: state rows 16J + 4g + j (registers only; sS is written
+    // after the next barrier).  Keys are read down the columns of sK; fast:
+    // S <- 2^Ltot (S + K^T V) with keys k 2^(-Lin); slow: the keys of token
+    // block I are rescaled to k 2^(Ltot - Lin) and S <- 2^Ltot S + K^T V.
     float tot4[4], dec[4];
     chunk_total4(sBT, 16 * J + 4 * g, tot4);
 #pragma unroll
@@ -983,13 +989,6 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) S[nt][j] *= dec[j];
-    if (OUT) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
-        wr4<SP>(sS, 1024 * nt + lo.s, x);
-      }
-    }
   }
 
 
@@ -1003,6 +1002,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
       const bool active = 16 * J < Lv;   // uniform in the wave
       const bool left = ch > 0 || have_S;
       lds_barrier();
+      if (OUT && left) publish_state();
 
       // ---- phase A: in-block scan, block totals, values
       float lin[2][8];
@@ -1025,12 +1025,8 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
       } else {
         fetch(ch + 1);
       }
-      lds_barrier();   // every wave has finished reading sS
 
-      // ---- phase D: state rows 16J + 4g + j.  Keys are read down the columns
-      // of sK; fast: S <- 2^Ltot (S + K^T V) with keys k 2^(-Lin); slow: the
-      // keys of token block I are rescaled to k 2^(Ltot - Lin) and
-      // S <- 2^Ltot S + K^T V.
+      // ---- phase D (slow), registers only as above
       float tot4[4], dec[4];
       chunk_total4(sBT, 16 * J + 4 * g, tot4);
   #pragma unroll
@@ -1057,13 +1053,6 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
         key = split8<SP>(x);
   #pragma unroll
         for (int nt = 0; nt < 4; ++nt) S[nt] = mma(key, rd8<SV>(sV, 1024 * nt + lo.a[ks]), S[nt]);
-      }
-      if (OUT) {
-  #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float x[4] = {S[nt][0], S[nt][1], S[nt][2], S[nt][3]};
-          wr4<SP>(sS, 1024 * nt + lo.s, x);
-        }
       }
     }
   }
