@@ -751,8 +751,27 @@ __device__ __forceinline__ void slow_chunk(const Params& p, char* lds, Raw<BF16>
 //   MODE kOutAcc: y += the sweep's outputs (y holds the reverse sweep's part).
 //   CARRY:        start from the state the earlier segments (in sweep order)
 //                 hand over, combined from their summaries.
+// Wave priority from the workgroup's progress through its item (done of
+// total chunk steps).  Workgroups sharing a CU otherwise advance oldest
+// first, and the last one finishes alone at low occupancy; lowering the
+// priority of a workgroup as it gets ahead keeps them level.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+  const int level = 3 - (4 * done) / total;
+  if (level >= 3)
+    __builtin_amdgcn_s_setprio(3);
+  else if (level == 2)
+    __builtin_amdgcn_s_setprio(2);
+  else if (level == 1)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// npass / pass: the item's number of sweeps and this sweep's place among
+// them (for progress_priority).
 template <bool BF16, bool REV, int MODE, bool CARRY, bool SLOW>
-__device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int seg) {
+__device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int seg, int npass = 1,
+                                      int pass = 0) {
   constexpr int SP = BF16 ? 2 : 3;
   constexpr int SV = BF16 ? 1 : 3;
   constexpr bool OUT = MODE != kState;
@@ -855,6 +874,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     const bool valid = tau < Lv;
     const bool active = 16 * J < Lv;   // uniform in the wave
     const bool left = ch > 0 || have_S;
+    progress_priority(pass * nch + ch, npass * nch);
     lds_barrier();
     if (OUT && left) publish_state();
 
@@ -1116,9 +1136,9 @@ __device__ __forceinline__ bool run_item(const Params& p, char* lds, int bh, int
     // the forward sweep runs even after the reverse one gave up (its result is
     // then recomputed anyway): one straight path keeps the registers of the
     // two sweeps apart
-    const bool ok = sweep<BF16, true, kOut, CARRY, SLOW>(p, lds, bh, seg);
+    const bool ok = sweep<BF16, true, kOut, CARRY, SLOW>(p, lds, bh, seg, 2, 0);
     __syncthreads();   // partial rows of y written; LDS free for reuse
-    return sweep<BF16, false, kOutAcc, CARRY, SLOW>(p, lds, bh, seg) && ok;
+    return sweep<BF16, false, kOutAcc, CARRY, SLOW>(p, lds, bh, seg, 2, 1) && ok;
   }
   return sweep<BF16, false, kOut, CARRY, SLOW>(p, lds, bh, seg);
 }
