@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define WKV6_ABI_VERSION 1
+#define WKV6_ABI_VERSION 2
 
 /* mode */
 #define WKV6_MODE_CAUSAL        0
@@ -101,6 +101,44 @@ extern "C" {
 int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H,
              const void* r, const void* k, const void* v, const void* w_raw,
              const float* u, float* y, int mode, int dtype, void* stream);
+
+/*
+ * wkv6_fwd_state -- a causal forward that starts from a given state and hands
+ * back the state after the last token, for processing a sequence in pieces
+ * (streaming, or decoding one token at a time).  The pages describe the
+ * state as the operator's whole memory, updated token by token and kept
+ * between calls at inference ("RWKV Architecture" on llms.blog, sections
+ * "The Recurrent Inference Formulation" and "RWKV-5 Eagle"; the yarian.com
+ * RWKV page, section "7. Hidden State = Persistent Memory").
+ *
+ * Same operator and arguments as wkv6_fwd in causal mode, except that the
+ * state starts at s_in instead of zero:
+ *
+ *     y_t[n] = sum_c r_t[c] * ( S[c][n] + u[c] * k_t[c] * v_t[n] )
+ *     S[c][n] <- w_t[c] * S[c][n] + k_t[c] * v_t[n],   S = s_in before token 0
+ *
+ * and s_out receives S after token T-1.  Splitting a sequence at any token
+ * and passing s_out of the first piece as s_in of the second gives the same
+ * y and final state as one call (up to rounding).
+ *
+ *   s_in    device pointer to B*H float32 64x64 states, [B, H, 64, 64]
+ *           row-major: element [b][h][c][n] is the state entry of key
+ *           channel c and value channel n of head h.  NULL: zero state.
+ *   s_out   device pointer to a [B, H, 64, 64] float32 output in the same
+ *           layout, or NULL (final state not wanted).  Must not overlap
+ *           s_in, y or any input: successive calls alternate two buffers.
+ *   T       may be 0: then y, r, k, v, w_raw and u are not used and s_out
+ *           (if given) receives s_in (zeros when s_in is NULL).
+ *
+ * Other arguments, ownership, execution and errors as for wkv6_fwd; the
+ * state pointers must be 16-byte aligned (MISALIGNED otherwise) and their
+ * overlaps give INVALID_ARG.  Bidirectional mode has no state passing (its
+ * later-token part needs the whole sequence).
+ */
+int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H,
+                   const void* r, const void* k, const void* v, const void* w_raw,
+                   const float* u, float* y, const float* s_in, float* s_out,
+                   int dtype, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* wkv6_status_str(int status);

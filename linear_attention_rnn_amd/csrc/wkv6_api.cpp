@@ -25,6 +25,87 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// Size, mode and dtype checks shared by the entry points.
+int check_sizes(int64_t B, int64_t T, int64_t C, int64_t H, int mode, int dtype) {
+  if (B < 0 || T < 0 || C < 0 || H < 1)
+    return fail(WKV6_ERR_INVALID_ARG, "sizes must be B, T, C >= 0 and H >= 1");
+  if (C % H != 0) return fail(WKV6_ERR_INVALID_ARG, "C must be a multiple of H");
+  if (mode != WKV6_MODE_CAUSAL && mode != WKV6_MODE_BIDIRECTIONAL)
+    return fail(WKV6_ERR_INVALID_ARG, "unknown mode");
+  if (dtype != WKV6_DTYPE_F32 && dtype != WKV6_DTYPE_BF16)
+    return fail(WKV6_ERR_INVALID_ARG, "unknown dtype");
+  if (C / H != wkv6::kHead) return fail(WKV6_ERR_UNSUPPORTED, "head size C/H must be 64");
+  if (B == 0 || T == 0) return WKV6_OK;
+  // the kernels address one (batch, head) slice with 32-bit byte offsets
+  if (T > INT_MAX - wkv6::kChunk || B * H > INT_MAX || B > INT64_MAX / T || B * T > INT64_MAX / (4 * C) ||
+      T > (INT_MAX - 4096) / (4 * C))
+    return fail(WKV6_ERR_UNSUPPORTED, "sizes exceed the supported index range");
+  return WKV6_OK;
+}
+
+// Pointer checks for a call with B, T > 0: present, aligned, y clear of the
+// inputs.
+int check_tensors(int64_t B, int64_t T, int64_t C, int dtype, const void* r, const void* k, const void* v,
+                  const void* w_raw, const float* u, const float* y) {
+  const void* ptrs[6] = {r, k, v, w_raw, u, y};
+  const char* names[6] = {"r", "k", "v", "w_raw", "u", "y"};
+  for (int i = 0; i < 6; ++i) {
+    if (!ptrs[i]) return fail(WKV6_ERR_INVALID_ARG, std::string("null pointer: ") + names[i]);
+  }
+  for (int i = 0; i < 6; ++i) {
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16)
+      return fail(WKV6_ERR_MISALIGNED, std::string("pointer not 16-byte aligned: ") + names[i]);
+  }
+  const size_t elems = (size_t)B * (size_t)T * (size_t)C;
+  const size_t isz = dtype == WKV6_DTYPE_BF16 ? 2 : 4;
+  const size_t ybytes = elems * 4;
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(y, ybytes, ptrs[i], elems * isz))
+      return fail(WKV6_ERR_INVALID_ARG, std::string("y overlaps ") + names[i]);
+  }
+  if (overlaps(y, ybytes, u, (size_t)C * 4)) return fail(WKV6_ERR_INVALID_ARG, "y overlaps u");
+  return WKV6_OK;
+}
+
+// Workspace (stream-ordered) and kernels.
+int run(const wkv6::FwdArgs& a, hipStream_t s) {
+  const size_t ws_bytes = wkv6::workspace_bytes(a);
+  void* ws = nullptr;
+  if (ws_bytes) {
+    const hipError_t e = hipMallocAsync(&ws, ws_bytes, s);
+    if (e != hipSuccess)
+      return fail(WKV6_ERR_HIP, std::string("workspace allocation: ") + hipGetErrorString(e));
+  }
+  const hipError_t e = wkv6::enqueue_fwd(a, ws, s);
+  if (ws) {
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e == hipSuccess && ef != hipSuccess)
+      return fail(WKV6_ERR_HIP, std::string("workspace release: ") + hipGetErrorString(ef));
+  }
+  if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return WKV6_OK;
+}
+
+wkv6::FwdArgs make_args(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k,
+                        const void* v, const void* w_raw, const float* u, float* y, int mode, int dtype) {
+  wkv6::FwdArgs a;
+  a.B = B;
+  a.T = T;
+  a.C = C;
+  a.H = H;
+  a.r = r;
+  a.k = k;
+  a.v = v;
+  a.w_raw = w_raw;
+  a.u = u;
+  a.y = y;
+  a.s_in = nullptr;
+  a.s_out = nullptr;
+  a.bidirectional = mode == WKV6_MODE_BIDIRECTIONAL;
+  a.bf16 = dtype == WKV6_DTYPE_BF16;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -48,67 +129,45 @@ int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const vo
              const void* v, const void* w_raw, const float* u, float* y, int mode, int dtype,
              void* stream) {
   g_last_error.clear();
-  if (B < 0 || T < 0 || C < 0 || H < 1)
-    return fail(WKV6_ERR_INVALID_ARG, "sizes must be B, T, C >= 0 and H >= 1");
-  if (C % H != 0) return fail(WKV6_ERR_INVALID_ARG, "C must be a multiple of H");
-  if (mode != WKV6_MODE_CAUSAL && mode != WKV6_MODE_BIDIRECTIONAL)
-    return fail(WKV6_ERR_INVALID_ARG, "unknown mode");
-  if (dtype != WKV6_DTYPE_F32 && dtype != WKV6_DTYPE_BF16)
-    return fail(WKV6_ERR_INVALID_ARG, "unknown dtype");
-  if (C / H != wkv6::kHead) return fail(WKV6_ERR_UNSUPPORTED, "head size C/H must be 64");
-  if (B == 0 || T == 0) return WKV6_OK;
-  // the kernels address one (batch, head) slice with 32-bit byte offsets
-  if (T > INT_MAX - wkv6::kChunk || B * H > INT_MAX || B > INT64_MAX / T || B * T > INT64_MAX / (4 * C) ||
-      T > (INT_MAX - 4096) / (4 * C))
+  int st = check_sizes(B, T, C, H, mode, dtype);
+  if (st != WKV6_OK || B == 0 || T == 0) return st;
+  if ((st = check_tensors(B, T, C, dtype, r, k, v, w_raw, u, y)) != WKV6_OK) return st;
+  return run(make_args(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype), static_cast<hipStream_t>(stream));
+}
+
+int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k,
+                   const void* v, const void* w_raw, const float* u, float* y, const float* s_in,
+                   float* s_out, int dtype, void* stream) {
+  g_last_error.clear();
+  int st = check_sizes(B, T, C, H, WKV6_MODE_CAUSAL, dtype);
+  if (st != WKV6_OK || B == 0) return st;
+  if (B * H > INT_MAX / wkv6::kHead / wkv6::kHead)
     return fail(WKV6_ERR_UNSUPPORTED, "sizes exceed the supported index range");
-  const void* ptrs[6] = {r, k, v, w_raw, u, y};
-  const char* names[6] = {"r", "k", "v", "w_raw", "u", "y"};
-  for (int i = 0; i < 6; ++i) {
-    if (!ptrs[i]) return fail(WKV6_ERR_INVALID_ARG, std::string("null pointer: ") + names[i]);
+  const size_t sbytes = (size_t)B * (size_t)H * wkv6::kHead * wkv6::kHead * 4;
+  if ((s_in && reinterpret_cast<uintptr_t>(s_in) % 16) || (s_out && reinterpret_cast<uintptr_t>(s_out) % 16))
+    return fail(WKV6_ERR_MISALIGNED, "state pointer not 16-byte aligned");
+  if (s_in && s_out && overlaps(s_in, sbytes, s_out, sbytes))
+    return fail(WKV6_ERR_INVALID_ARG, "s_out overlaps s_in");
+  if (T > 0) {
+    if ((st = check_tensors(B, T, C, dtype, r, k, v, w_raw, u, y)) != WKV6_OK) return st;
+    const size_t elems = (size_t)B * (size_t)T * (size_t)C;
+    const size_t isz = dtype == WKV6_DTYPE_BF16 ? 2 : 4;
+    if (s_in && overlaps(y, elems * 4, s_in, sbytes)) return fail(WKV6_ERR_INVALID_ARG, "y overlaps s_in");
+    if (s_out) {
+      const void* ins[5] = {r, k, v, w_raw, y};
+      const size_t nb[5] = {elems * isz, elems * isz, elems * isz, elems * isz, elems * 4};
+      const char* names[5] = {"r", "k", "v", "w_raw", "y"};
+      for (int i = 0; i < 5; ++i) {
+        if (overlaps(s_out, sbytes, ins[i], nb[i]))
+          return fail(WKV6_ERR_INVALID_ARG, std::string("s_out overlaps ") + names[i]);
+      }
+      if (overlaps(s_out, sbytes, u, (size_t)C * 4)) return fail(WKV6_ERR_INVALID_ARG, "s_out overlaps u");
+    }
   }
-  for (int i = 0; i < 6; ++i) {
-    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16)
-      return fail(WKV6_ERR_MISALIGNED, std::string("pointer not 16-byte aligned: ") + names[i]);
-  }
-  const size_t elems = (size_t)B * (size_t)T * (size_t)C;
-  const size_t isz = dtype == WKV6_DTYPE_BF16 ? 2 : 4;
-  const size_t ybytes = elems * 4;
-  for (int i = 0; i < 4; ++i) {
-    if (overlaps(y, ybytes, ptrs[i], elems * isz))
-      return fail(WKV6_ERR_INVALID_ARG, std::string("y overlaps ") + names[i]);
-  }
-  if (overlaps(y, ybytes, u, (size_t)C * 4)) return fail(WKV6_ERR_INVALID_ARG, "y overlaps u");
-
-  wkv6::FwdArgs a;
-  a.B = B;
-  a.T = T;
-  a.C = C;
-  a.H = H;
-  a.r = r;
-  a.k = k;
-  a.v = v;
-  a.w_raw = w_raw;
-  a.u = u;
-  a.y = y;
-  a.bidirectional = mode == WKV6_MODE_BIDIRECTIONAL;
-  a.bf16 = dtype == WKV6_DTYPE_BF16;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  const size_t ws_bytes = wkv6::workspace_bytes(a);
-  void* ws = nullptr;
-  if (ws_bytes) {
-    const hipError_t e = hipMallocAsync(&ws, ws_bytes, s);
-    if (e != hipSuccess)
-      return fail(WKV6_ERR_HIP, std::string("workspace allocation: ") + hipGetErrorString(e));
-  }
-  const hipError_t e = wkv6::enqueue_fwd(a, ws, s);
-  if (ws) {
-    const hipError_t ef = hipFreeAsync(ws, s);
-    if (e == hipSuccess && ef != hipSuccess)
-      return fail(WKV6_ERR_HIP, std::string("workspace release: ") + hipGetErrorString(ef));
-  }
-  if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
-  return WKV6_OK;
+  wkv6::FwdArgs a = make_args(B, T, C, H, r, k, v, w_raw, u, y, WKV6_MODE_CAUSAL, dtype);
+  a.s_in = s_in;
+  a.s_out = s_out;
+  return run(a, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

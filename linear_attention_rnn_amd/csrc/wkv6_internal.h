@@ -19,6 +19,8 @@ struct FwdArgs {
   const void* w_raw;
   const float* u;
   float* y;
+  const float* s_in;   // causal only: initial state [B*H][64][64] or null (zero)
+  float* s_out;        // causal only: final state, same layout, or null
   bool bidirectional;
   bool bf16;
 };
@@ -26,8 +28,9 @@ struct FwdArgs {
 // Bytes of device workspace a call needs (0 when none).
 size_t workspace_bytes(const FwdArgs& a);
 
-// Enqueue the kernels on `stream`.  `workspace` must hold workspace_bytes(a)
-// bytes (or be null when that is 0).  Returns the first HIP error, if any.
+// Enqueue the kernels on `stream` (T == 0: only the state copy, if any).
+// `workspace` must hold workspace_bytes(a) bytes (or be null when that is 0).
+// Returns the first HIP error, if any.
 hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace wkv6

@@ -102,6 +102,8 @@ struct Params {
   const float* u;
   float* y;
   float* summ;   // [B*H][G][direction]{S^T[64][64], g[64]} when G > 1
+  const float* s_in;   // causal: state entering token 0, [B*H][64][64] (row c, column n), or null
+  float* s_out;        // causal: state after the last token, same layout, or null
   int64_t T;
   int64_t C;
   int H;
@@ -811,6 +813,15 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool have_S = false;
+  // causal calls may start from a given state (the forward sweep only)
+  if (!REV && MODE != kState && p.s_in) {
+    const float* si = p.s_in + (int64_t)bh * PL;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[nt][j] = si[(16 * J + 4 * g + j) * HS + 16 * nt + li];
+    have_S = true;
+  }
   if (CARRY) {
     // (g1, S1) o (g2, S2) = (g1 + g2, 2^g2 S1 + S2) over the earlier segments
     const int nprev = REV ? p.G - 1 - seg : seg;
@@ -829,9 +840,12 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
         S[nt][3] = S[nt][3] * gj[3] + f.w;
       }
     }
-    have_S = nprev > 0;
+    have_S = have_S || nprev > 0;
   }
   float gsum[4] = {0.f, 0.f, 0.f, 0.f};   // kState: total log2 decay of the state rows
+  // the sweep that ends at the sequence's last token also updates the state
+  // with the last chunk when the caller wants the final state
+  const bool keep_state = !REV && MODE != kState && p.s_out && seg == p.G - 1;
 
   // The state entering a chunk goes to sS (pre-split) right after the chunk's
   // first barrier: every wave has then finished the previous chunk's phase C,
@@ -979,7 +993,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
       for (int nt = 0; nt < 4; ++nt) bstoref4(ry, yoff + 64 * nt, Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
     }
     if (ch == nch - 1) {
-      if (OUT) {
+      if (OUT && !keep_state) {
         ch = nch;
         break;
       }
@@ -1041,7 +1055,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
                                    valid ? y_row0 + ch * y_step : kOffNone, Lv,
                                    left);
       if (ch == nch - 1) {
-        if (OUT) break;
+        if (OUT && !keep_state) break;
       } else {
         fetch(ch + 1);
       }
@@ -1085,6 +1099,13 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
           make_float4(S[nt][0], S[nt][1], S[nt][2], S[nt][3]);
     if (li == 0)
       *reinterpret_cast<float4*>(dst + PL + 16 * J + 4 * g) = make_float4(gsum[0], gsum[1], gsum[2], gsum[3]);
+  }
+  if (keep_state) {
+    float* so = p.s_out + (int64_t)bh * PL;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) so[(16 * J + 4 * g + j) * HS + 16 * nt + li] = S[nt][j];
   }
   return true;
 }
@@ -1192,6 +1213,13 @@ __global__ __launch_bounds__(NT, 2) void summary_fixup_kernel(Params p) {
     sweep<BF16, false, kState, false, true>(p, lds, bh, seg);
 }
 
+// State passing through an empty sequence: s_out = s_in (zero without s_in).
+__global__ __launch_bounds__(NT) void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                       int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT)
+    dst[i] = src ? src[i] : 0.f;
+}
+
 struct Plan {
   int NC, G, SEGC;
 };
@@ -1224,6 +1252,8 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   p.u = a.u;
   p.y = a.y;
   p.summ = static_cast<float*>(ws);
+  p.s_in = a.s_in;
+  p.s_out = a.s_out;
   p.T = a.T;
   p.C = a.C;
   p.H = (int)a.H;
@@ -1255,12 +1285,21 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
 }  // namespace
 
 size_t workspace_bytes(const FwdArgs& a) {
+  if (a.T == 0) return 0;
   const Plan pl = plan(a);
   if (pl.G == 1) return 0;
   return (size_t)a.B * a.H * pl.G * 2 * kSummFloats * sizeof(float);
 }
 
 hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream) {
+  if (a.T == 0) {
+    if (!a.s_out) return hipSuccess;
+    const int64_t n = a.B * a.H * PL;
+    const int64_t nblk = (n + NT - 1) / NT;
+    const unsigned grid = (unsigned)(nblk < 1024 ? nblk : 1024);
+    hipLaunchKernelGGL(state_copy_kernel, dim3(grid), dim3(NT), 0, stream, a.s_in, a.s_out, n);
+    return hipGetLastError();
+  }
   const Plan pl = plan(a);
   if (a.bf16)
     return a.bidirectional ? launch_t<true, true>(a, pl, workspace, stream)

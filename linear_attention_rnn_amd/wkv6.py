@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
         L.wkv6_fwd.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
                                ctypes.c_int, ctypes.c_int, vp]
         L.wkv6_fwd.restype = ctypes.c_int
+        L.wkv6_fwd_state.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_int, vp]
+        L.wkv6_fwd_state.restype = ctypes.c_int
         L.wkv6_status_str.argtypes = [ctypes.c_int]
         L.wkv6_status_str.restype = ctypes.c_char_p
         L.wkv6_last_error.argtypes = []
@@ -84,17 +87,15 @@ def fwd_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, 
     return lib().wkv6_fwd(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype, stream)
 
 
-def fwd(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
-    """y = WKV6(r, k, v, w_raw, u) on the GPU.
+def fwd_state_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, u: int,
+                  y: int, s_in: int, s_out: int, dtype: int, stream: int = 0) -> int:
+    """Direct call of wkv6_fwd_state with integer addresses (0 = NULL)."""
+    return lib().wkv6_fwd_state(B, T, C, H, r, k, v, w_raw, u, y, s_in, s_out, dtype, stream)
 
-    r, k, v, w_raw: contiguous CUDA tensors [B, T, C] of one dtype (float32 or
-    bfloat16); u: contiguous float32 [C]; returns (or fills ``out``) a float32
-    [B, T, C] tensor.  Runs on ``stream`` (default: torch's current stream).
-    """
+
+def _check_inputs(r, k, v, w_raw, u):
     import torch
 
-    if mode not in _MODES:
-        raise ValueError(f"mode must be one of {sorted(_MODES)}")
     if r.dim() != 3:
         raise ValueError("r must be [B, T, C]")
     B, T, C = r.shape
@@ -112,15 +113,69 @@ def fwd(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
     for name, t in (("r", r), ("k", k), ("v", v), ("w_raw", w_raw), ("u", u)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return B, T, C, dtype
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def fwd_state(r, k, v, w_raw, u, H: int, s_in=None, want_state: bool = True, out=None,
+              s_out=None, stream=None):
+    """Causal y = WKV6(r, k, v, w_raw, u) starting from state ``s_in``.
+
+    s_in: None (zero state) or a contiguous float32 CUDA tensor [B, H, 64, 64]
+    (entry [b, h, c, n]: key channel c, value channel n).  Returns (y, s_out)
+    with s_out the state after the last token (None if ``want_state`` is
+    false and no ``s_out`` buffer is given).
+    """
+    import torch
+
+    B, T, C, dtype = _check_inputs(r, k, v, w_raw, u)
+    shape = (B, H, 64, 64)
+    if s_in is not None and (s_in.shape != shape or s_in.dtype != torch.float32 or not s_in.is_cuda
+                             or not s_in.is_contiguous()):
+        raise ValueError("s_in must be a contiguous float32 GPU tensor [B, H, 64, 64]")
     if out is None:
         out = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
     elif out.shape != (B, T, C) or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(r.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if s_out is None and want_state:
+        s_out = torch.empty(shape, dtype=torch.float32, device=r.device)
+    elif s_out is not None and (s_out.shape != shape or s_out.dtype != torch.float32
+                                or not s_out.is_contiguous()):
+        raise ValueError("s_out must be a contiguous float32 [B, H, 64, 64] tensor")
+    st = fwd_state_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
+                       u.data_ptr(), out.data_ptr(), 0 if s_in is None else s_in.data_ptr(),
+                       0 if s_out is None else s_out.data_ptr(), dtype,
+                       _stream_handle(stream, r.device))
+    if st != OK:
+        raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
+    return out, s_out
+
+
+def fwd(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
+    """y = WKV6(r, k, v, w_raw, u) on the GPU.
+
+    r, k, v, w_raw: contiguous CUDA tensors [B, T, C] of one dtype (float32 or
+    bfloat16); u: contiguous float32 [C]; returns (or fills ``out``) a float32
+    [B, T, C] tensor.  Runs on ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    B, T, C, dtype = _check_inputs(r, k, v, w_raw, u)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
+    elif out.shape != (B, T, C) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
     st = fwd_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
-                 u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, handle)
+                 u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, _stream_handle(stream, r.device))
     if st != OK:
         raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
     return out

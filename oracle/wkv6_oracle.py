@@ -30,11 +30,20 @@ contiguous channels [h*N, (h+1)*N) of the [B, T, C] tensors, C = H*N):
   only in the past-to-future sweep and that the first sweep gathers the
   future tokens.)  The two sweeps' contributions are summed.
 
+* state passing (causal only): the state is the operator's entire memory,
+  updated token by token and kept between calls at inference ("RWKV
+  Architecture" page, section "The Recurrent Inference Formulation"; the
+  yarian.com RWKV page, section "7. Hidden State = Persistent Memory").  So a
+  causal call may start from a given state S instead of zero and hand back
+  the state after its last token; cutting a sequence anywhere and passing the
+  state across the cut changes nothing.
+
 Readings taken where the pages are silent or garbled are the ones the test
 suite pins: decay exp(-exp(w_raw)) (one page's example code writes exp(w),
 which would give decays above one and is taken as garbled); the
 future-to-past sum is exclusive of the current token; the initial states are
-zero; u has one value per channel; the output is always float32-or-wider.
+zero unless a causal call passes one; u has one value per channel; the
+output is always float32-or-wider.
 """
 from __future__ import annotations
 
@@ -70,10 +79,25 @@ def merge_heads(x) -> np.ndarray:
     return np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(B, T, H * N))
 
 
-def wkv6_ref(r, k, v, w_raw, u, H: int, mode: str = "causal") -> np.ndarray:
+def _state_arg(state_in, B: int, H: int, N: int, bidir: bool, return_state: bool) -> np.ndarray:
+    if bidir and (state_in is not None or return_state):
+        raise ValueError("state passing is defined for causal mode only")
+    if state_in is None:
+        return np.zeros((B, H, N, N), dtype=np.float64)
+    S = np.array(state_in, dtype=np.float64)   # a copy
+    if S.shape != (B, H, N, N):
+        raise ValueError(f"state_in must be [B, H, N, N] = {(B, H, N, N)}, got {S.shape}")
+    return S
+
+
+def wkv6_ref(r, k, v, w_raw, u, H: int, mode: str = "causal", state_in=None,
+             return_state: bool = False):
     """Recurrent float64 evaluation; returns y as [B, T, C] float64.
 
     Loops over t in Python, vectorised over (b, h); O(B*H*T*N^2) work.
+    Causal mode may start from ``state_in`` ([B, H, N, N], entry [b, h, c, n]
+    for key channel c and value channel n; zero if None); with
+    ``return_state`` it returns (y, state after the last token).
     """
     bidir = _check_mode(mode)
     R = split_heads(r, H)
@@ -83,7 +107,7 @@ def wkv6_ref(r, k, v, w_raw, u, H: int, mode: str = "causal") -> np.ndarray:
     B, Hh, T, N = R.shape
     U = np.asarray(u, dtype=np.float64).reshape(Hh, N)
     Y = np.zeros((B, Hh, T, N), dtype=np.float64)
-    S = np.zeros((B, Hh, N, N), dtype=np.float64)   # S[b, h, c, n]
+    S = _state_arg(state_in, B, Hh, N, bidir, return_state)   # S[b, h, c, n]
     for t in range(T):
         kv = K[:, :, t, :, None] * V[:, :, t, None, :]
         # y_t = r_t . (S + diag(u) kv)
@@ -91,6 +115,8 @@ def wkv6_ref(r, k, v, w_raw, u, H: int, mode: str = "causal") -> np.ndarray:
         Y[:, :, t, :] = (R[:, :, t, None, :] @ S)[:, :, 0, :] + bonus[..., None] * V[:, :, t, :]
         S *= W[:, :, t, :, None]
         S += kv
+    if return_state:
+        return merge_heads(Y), S
     if bidir:
         S[...] = 0.0
         for t in range(T - 1, -1, -1):
@@ -100,12 +126,13 @@ def wkv6_ref(r, k, v, w_raw, u, H: int, mode: str = "causal") -> np.ndarray:
     return merge_heads(Y)
 
 
-def wkv6_bruteforce(r, k, v, w_raw, u, H: int, mode: str = "causal") -> np.ndarray:
+def wkv6_bruteforce(r, k, v, w_raw, u, H: int, mode: str = "causal", state_in=None) -> np.ndarray:
     """Explicit pairwise sum: y_t[n] = sum_{i} sum_c r_t[c] g_{t,i}[c] k_i[c] v_i[n]
     with g_{t,t} = u, g_{t,i} = prod of w_j over j strictly between i and t
     (formed factor by factor, an empty product being one), i < t only in
-    causal mode.  No running state; O(T^3 N + T^2 N^2) per (b, h).  Intended
-    for T of a few tokens."""
+    causal mode.  A causal ``state_in`` S0 adds
+    sum_c r_t[c] (prod_{j<t} w_j[c]) S0[c, n].  No running state;
+    O(T^3 N + T^2 N^2) per (b, h).  Intended for T of a few tokens."""
     bidir = _check_mode(mode)
     R = split_heads(r, H)
     K = split_heads(k, H)
@@ -127,4 +154,11 @@ def wkv6_bruteforce(r, k, v, w_raw, u, H: int, mode: str = "causal") -> np.ndarr
                 continue
             coef = (R[:, :, t, :] * g * K[:, :, i, :]).sum(-1)      # [B, H]
             Y[:, :, t, :] += coef[..., None] * V[:, :, i, :]
+    if state_in is not None:
+        S0 = _state_arg(state_in, B, Hh, N, bidir, False)
+        for t in range(T):
+            g = np.ones((B, Hh, N), dtype=np.float64)
+            for j in range(t):
+                g = g * W[:, :, j, :]
+            Y[:, :, t, :] += np.einsum("bhc,bhc,bhcn->bhn", R[:, :, t, :], g, S0)
     return merge_heads(Y)

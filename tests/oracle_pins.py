@@ -292,3 +292,88 @@ def violated_pins(impl, brute=None):
             bad.append("bruteforce")
     return bad
 
+
+
+# ------------------------------------------------------- state passing pins
+#
+# For causal calls that start from a given state and return the final state
+# ("RWKV Architecture" page, section "The Recurrent Inference Formulation":
+# the state is all the operator keeps between steps).  Each ``spin_*`` takes
+# ``impl_state(r, k, v, w_raw, u, H, S0) -> (y, S_end)`` with S0 of shape
+# [B, H, N, N] (entry [b, h, c, n]: key channel c, value channel n).
+
+def draw_state(B, H, N, seed):
+    return np.random.default_rng(seed).normal(size=(B, H, N, N))
+
+
+def spin_state_alone(impl_state):
+    """k = 0 (nothing is added): S0 only decays.  y_t = r_t diag(prod_{j<t} w_j) S0
+    and S_end = diag(prod_{all j} w_j) S0, with the products formed here by an
+    exclusive cumulative product over time."""
+    for seed, (B, T, C, H) in enumerate([(1, 5, 4, 1), (2, 6, 8, 2), (1, 3, 64, 1)]):
+        r, k, v, w_raw, u = draw(B, T, C, H, 200 + seed)
+        k = np.zeros_like(k)
+        N = C // H
+        S0 = draw_state(B, H, N, 300 + seed)
+        W = np.exp(-np.exp(heads(w_raw, H)))                        # [B, T, H, N]
+        P = np.concatenate([np.ones((B, 1, H, N)), np.cumprod(W, axis=1)[:, :-1]], axis=1)
+        expect = np.einsum("bthc,bthc,bhcn->bthn", heads(r, H), P, S0).reshape(B, T, C)
+        S_expect = np.prod(W, axis=1)[..., None] * S0
+        y, S_end = impl_state(r, k, v, w_raw, u, H, S0)
+        close(y, expect, what=f"state alone y {(B, T, C, H)}")
+        close(S_end, S_expect, what=f"state alone S_end {(B, T, C, H)}")
+
+
+def spin_state_superposition(impl_state):
+    """The state's contribution is separate from the tokens': the result from
+    S0 equals the result from zero plus the result of S0 alone (k = 0); the
+    same holds for the final state."""
+    for seed, (B, T, C, H) in enumerate([(2, 7, 8, 2), (1, 4, 64, 1)]):
+        r, k, v, w_raw, u = draw(B, T, C, H, 210 + seed)
+        S0 = draw_state(B, H, C // H, 310 + seed)
+        y, S = impl_state(r, k, v, w_raw, u, H, S0)
+        y0, S0end = impl_state(r, k, v, w_raw, u, H, np.zeros_like(S0))
+        ys, Ss = impl_state(r, np.zeros_like(k), v, w_raw, u, H, S0)
+        close(y, y0 + ys, what="superposition y")
+        close(S, S0end + Ss, what="superposition S_end")
+
+
+def spin_state_split(impl_state):
+    """Cutting the sequence anywhere and passing the state across the cut gives
+    the same y and final state (a property of any recurrence on a state)."""
+    for seed, (B, T, C, H) in enumerate([(2, 9, 8, 2), (1, 6, 64, 1)]):
+        r, k, v, w_raw, u = draw(B, T, C, H, 220 + seed)
+        S0 = draw_state(B, H, C // H, 320 + seed)
+        y, S_end = impl_state(r, k, v, w_raw, u, H, S0)
+        for cut in range(0, T + 1):
+            a = [x[:, :cut] for x in (r, k, v, w_raw)]
+            b = [x[:, cut:] for x in (r, k, v, w_raw)]
+            y1, S1 = impl_state(*a, u, H, S0)
+            y2, S2 = impl_state(*b, u, H, S1)
+            close(np.concatenate([y1, y2], axis=1), y, what=f"split at {cut}: y")
+            close(S2, S_end, what=f"split at {cut}: S_end")
+
+
+def spin_state_zero_is_stateless(impl_state, impl):
+    """A zero initial state gives the stateless causal result."""
+    for seed, (B, T, C, H) in enumerate([(2, 6, 8, 2), (1, 5, 64, 1)]):
+        r, k, v, w_raw, u = draw(B, T, C, H, 230 + seed)
+        y, _ = impl_state(r, k, v, w_raw, u, H, np.zeros((B, H, C // H, C // H)))
+        close(y, impl(r, k, v, w_raw, u, H, "causal"), what="zero state")
+
+
+STATE_PINS = {
+    "state_alone": spin_state_alone,
+    "state_superposition": spin_state_superposition,
+    "state_split": spin_state_split,
+}
+
+
+def violated_state_pins(impl_state):
+    bad = []
+    for name, pin in STATE_PINS.items():
+        try:
+            pin(impl_state)
+        except (AssertionError, FloatingPointError, ValueError):
+            bad.append(name)
+    return bad

@@ -18,7 +18,8 @@ A = 0x10000  # fake, 16-byte aligned addresses: never dereferenced by these call
 
 def test_exports_every_declared_function():
     names = wkv6.header_functions()
-    assert set(names) == {"wkv6_fwd", "wkv6_status_str", "wkv6_last_error", "wkv6_abi_version"}
+    assert set(names) == {"wkv6_fwd", "wkv6_fwd_state", "wkv6_status_str", "wkv6_last_error",
+                          "wkv6_abi_version"}
     L = wkv6.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -26,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert wkv6.abi_version() == 1
+    assert wkv6.abi_version() == 2
     assert wkv6.status_str(0) == "ok"
     texts = {wkv6.status_str(s) for s in range(5)}
     assert len(texts) == 5
@@ -83,3 +84,43 @@ def test_output_overlapping_an_input(which):
     p[5] = p[which] + 16
     assert _call(ptrs=p) == wkv6.ERR_INVALID_ARG
     assert "overlaps" in wkv6.last_error()
+
+
+# ---- wkv6_fwd_state: the same checks plus the state buffers
+S_IN, S_OUT = A + 0x600000, A + 0x700000
+
+
+def _call_state(B=2, T=8, C=128, H=2, ptrs=None, s_in=S_IN, s_out=S_OUT, dtype=0):
+    p = ptrs or [A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000]
+    return wkv6.fwd_state_raw(B, T, C, H, *p, s_in, s_out, dtype, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), wkv6.ERR_INVALID_ARG),
+    (dict(H=0), wkv6.ERR_INVALID_ARG),
+    (dict(dtype=7), wkv6.ERR_INVALID_ARG),
+    (dict(C=96, H=2), wkv6.ERR_UNSUPPORTED),
+    (dict(s_in=S_IN + 8), wkv6.ERR_MISALIGNED),
+    (dict(s_out=S_OUT + 4), wkv6.ERR_MISALIGNED),
+    (dict(s_out=S_IN + 64), wkv6.ERR_INVALID_ARG),           # s_out overlaps s_in
+    (dict(s_out=A + 0x500000 + 16), wkv6.ERR_INVALID_ARG),   # s_out overlaps y
+    (dict(s_out=A + 0x100000), wkv6.ERR_INVALID_ARG),        # s_out overlaps k
+    (dict(s_in=A + 0x500000 + 32), wkv6.ERR_INVALID_ARG),    # y overlaps s_in
+    (dict(T=2 ** 31), wkv6.ERR_UNSUPPORTED),
+])
+def test_state_call_rejects_bad_arguments(kw, status):
+    assert _call_state(**kw) == status
+    assert wkv6.last_error() != ""
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_state_call_null_tensor(which):
+    p = [A + 0x100000 * i for i in range(6)]
+    p[which] = 0
+    assert _call_state(ptrs=p) == wkv6.ERR_INVALID_ARG
+
+
+def test_state_call_empty_batch_is_a_noop():
+    assert _call_state(B=0, ptrs=[0] * 6, s_in=0, s_out=0) == wkv6.OK
+    assert _call_state(T=0, ptrs=[0] * 6, s_in=0, s_out=0) == wkv6.OK   # nothing to copy
+    assert wkv6.last_error() == ""

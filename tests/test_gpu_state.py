@@ -1,0 +1,181 @@
+"""Parity of wkv6_fwd_state (a causal forward that starts from a given state
+and returns the final state) with the float64 oracle, through the C ABI.
+
+Same tolerances as the other parity tests, max|x - x_ref| / rms(x_ref) for y
+and for the final state: 1e-4 with float32 inputs, 5e-3 with bfloat16 inputs.
+"""
+import numpy as np
+import pytest
+
+from linear_attention_rnn_amd import inputs as I
+from oracle import wkv6_ref
+from tests.gpu_util import device_inputs, err_over_rms, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 5e-3}
+
+# slow decays (w_raw in [-9, -3]) so that the initial state still matters at
+# the end of the longest sequences here
+SLOW = dict(wraw_lo=-9.0, wraw_hi=-3.0)
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def state_of(B, H, seed, scale=1.0):
+    """A float32 state [B, H, 64, 64] (float32 values, so both sides see the same)."""
+    return (np.random.default_rng(seed).normal(size=(B, H, 64, 64)) * scale).astype(np.float32)
+
+
+def run_state(x, H, dtype, S0=None, want=True):
+    import torch
+    from linear_attention_rnn_amd import wkv6
+
+    d = device_inputs(x, dtype)
+    s_in = None if S0 is None else torch.from_numpy(np.ascontiguousarray(S0, np.float32)).cuda()
+    y, S = wkv6.fwd_state(*d, H, s_in=s_in, want_state=want)
+    torch.cuda.synchronize()
+    return y.double().cpu().numpy(), None if S is None else S.double().cpu().numpy()
+
+
+def ref_state(x, H, S0):
+    return wkv6_ref(x["r"], x["k"], x["v"], x["w_raw"], x["u"], H, "causal", state_in=S0, return_state=True)
+
+
+def check(tag, y, S, y_ref, S_ref, dtype):
+    ey, es = err_over_rms(y, y_ref), err_over_rms(S, S_ref)
+    say(f"[state] {tag}: y {ey:.3e}  final state {es:.3e}")
+    assert ey <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 257])
+def test_state_in_out(torch_cuda, T, dtype):
+    B, H = 2, 3
+    x = I.random_inputs(B, T, 64 * H, H, seed=2000 + T, dtype=dtype, **SLOW)
+    S0 = state_of(B, H, 3000 + T)
+    y, S = run_state(x, H, dtype, S0)
+    y_ref, S_ref = ref_state(x, H, S0)
+    check(f"T={T} {dtype}", y, S, y_ref, S_ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_state_matches_plain_call(torch_cuda, dtype):
+    """No initial state: the same y as wkv6_fwd in causal mode, bit for bit
+    (the same kernels run), plus the final state."""
+    from tests.gpu_util import gpu_fwd
+
+    B, T, H = 2, 200, 2
+    x = I.random_inputs(B, T, 64 * H, H, seed=41, dtype=dtype, **SLOW)
+    y, S = run_state(x, H, dtype, None)
+    assert np.array_equal(y, gpu_fwd(x, H, "causal", dtype))
+    y_ref, S_ref = ref_state(x, H, None)
+    check(f"zero state {dtype}", y, S, y_ref, S_ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_with_segments(torch_cuda, monkeypatch, dtype):
+    """Few (batch, head) pairs and a long sequence: each sequence is cut into
+    segments; the initial state enters every segment's carry and the last
+    segment hands back the final state."""
+    B, H, T = 1, 2, 64 * 9 + 7
+    # very slow decays: the initial state is a large part of the final one
+    x = I.random_inputs(B, T, 64 * H, H, seed=43, dtype=dtype, wraw_lo=-12.0, wraw_hi=-6.0)
+    S0 = state_of(B, H, 44)
+    y_ref, S_ref = ref_state(x, H, S0)
+    outs = {}
+    for G in (None, 1, 3, 7):
+        if G is None:
+            monkeypatch.delenv("WKV6_SEGMENTS", raising=False)
+        else:
+            monkeypatch.setenv("WKV6_SEGMENTS", str(G))
+        y, S = run_state(x, H, dtype, S0)
+        outs[G] = (y, S)
+        check(f"segments {G or 'default'} {dtype}", y, S, y_ref, S_ref, dtype)
+    # the carries really ran: other segment counts round differently
+    assert not np.array_equal(outs[1][0], outs[7][0]) and not np.array_equal(outs[1][1], outs[7][1])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_invariance_on_gpu(torch_cuda, dtype):
+    """Cutting a sequence (at chunk boundaries or not) and passing the state
+    across the cut gives the single call's y and final state."""
+    B, H, T = 2, 2, 300
+    x = I.random_inputs(B, T, 64 * H, H, seed=45, dtype=dtype, **SLOW)
+    S0 = state_of(B, H, 46)
+    y_one, S_one = run_state(x, H, dtype, S0)
+    y_ref, S_ref = ref_state(x, H, S0)
+    for cut in (0, 1, 64, 100, 192, 299, 300):
+        a = {key: (val[:, :cut] if val.ndim == 3 else val) for key, val in x.items()}
+        b = {key: (val[:, cut:] if val.ndim == 3 else val) for key, val in x.items()}
+        y1, S1 = run_state(a, H, dtype, S0)
+        y2, S2 = run_state(b, H, dtype, S1.astype(np.float32))
+        y = np.concatenate([y1, y2], axis=1)
+        check(f"cut {cut} {dtype}", y, S2, y_ref, S_ref, dtype)
+        scale_y, scale_s = float(np.sqrt(np.mean(y_one ** 2))), float(np.sqrt(np.mean(S_one ** 2)))
+        assert np.max(np.abs(y - y_one)) / scale_y <= TOL[dtype]
+        assert np.max(np.abs(S2 - S_one)) / scale_s <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_by_token_decode(torch_cuda, dtype):
+    """One token per call, the state carried between calls, equals the
+    whole-sequence result."""
+    B, H, T = 3, 2, 12
+    x = I.random_inputs(B, T, 64 * H, H, seed=47, dtype=dtype, **SLOW)
+    S0 = state_of(B, H, 48, scale=0.3)
+    S = S0
+    ys = []
+    for t in range(T):
+        xt = {key: (val[:, t:t + 1] if val.ndim == 3 else val) for key, val in x.items()}
+        yt, S = run_state(xt, H, dtype, S)
+        S = S.astype(np.float32)
+        ys.append(yt)
+    y_ref, S_ref = ref_state(x, H, S0)
+    check(f"decode {dtype}", np.concatenate(ys, axis=1), S, y_ref, S_ref, dtype)
+
+
+def test_empty_sequence_passes_the_state(torch_cuda):
+    torch = torch_cuda
+    from linear_attention_rnn_amd import wkv6
+
+    B, H = 2, 2
+    z = torch.zeros((B, 0, 64 * H), device="cuda")
+    u = torch.zeros(64 * H, device="cuda")
+    S0 = torch.from_numpy(state_of(B, H, 49)).cuda()
+    y, S = wkv6.fwd_state(z, z, z, z, u, H, s_in=S0)
+    torch.cuda.synchronize()
+    assert y.shape == (B, 0, 64 * H)
+    assert torch.equal(S, S0)
+    _, S = wkv6.fwd_state(z, z, z, z, u, H, s_in=None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S).item() == 0
+
+
+def test_state_in_without_state_out(torch_cuda):
+    B, H, T = 2, 2, 90
+    x = I.random_inputs(B, T, 64 * H, H, seed=50, dtype="f32", **SLOW)
+    S0 = state_of(B, H, 51)
+    y, S = run_state(x, H, "f32", S0, want=False)
+    assert S is None
+    y_ref, _ = ref_state(x, H, S0)
+    assert err_over_rms(y, y_ref) <= TOL["f32"]
+
+
+def test_state_through_the_slow_path(torch_cuda):
+    """Decays fast enough that chunks take the general path (the fix-up
+    recomputation) must also start from the given state and hand it back."""
+    B, H, T = 2, 2, 200
+    x = I.random_inputs(B, T, 64 * H, H, seed=52, dtype="f32")
+    rng = np.random.default_rng(53)
+    x["w_raw"] = rng.choice(np.array([-9.0, -0.5, 1.0, 1.5], np.float32), size=x["w_raw"].shape)
+    S0 = state_of(B, H, 54)
+    y, S = run_state(x, H, "f32", S0)
+    y_ref, S_ref = ref_state(x, H, S0)
+    check("slow path f32", y, S, y_ref, S_ref, "f32")

@@ -125,3 +125,77 @@ def test_unmutated_copy_holds_all_pins():
 def test_planted_mistake_is_caught(kind):
     bad = P.violated_pins(_mutant(kind))
     assert bad, f"mutant {kind} passed every pin"
+
+
+# ------------------------------------------------------------ state passing
+
+def _ref_state(r, k, v, w_raw, u, H, S0):
+    return wkv6_ref(r, k, v, w_raw, u, H, "causal", state_in=S0, return_state=True)
+
+
+@pytest.mark.parametrize("name", sorted(P.STATE_PINS))
+def test_oracle_holds_state_pin(name):
+    P.STATE_PINS[name](_ref_state)
+
+
+def test_oracle_zero_state_is_stateless():
+    P.spin_state_zero_is_stateless(_ref_state, wkv6_ref)
+
+
+def test_bruteforce_with_state_matches_oracle():
+    """The explicit pairwise sum with an initial state (its own formula for
+    the state term) agrees with the recurrence, and holds the closed form."""
+    for seed, (B, T, C, H) in enumerate([(1, 1, 2, 1), (2, 5, 4, 2), (1, 6, 64, 1)]):
+        r, k, v, w_raw, u = P.draw(B, T, C, H, 400 + seed)
+        S0 = P.draw_state(B, H, C // H, 500 + seed)
+        P.close(wkv6_bruteforce(r, k, v, w_raw, u, H, "causal", state_in=S0),
+                _ref_state(r, k, v, w_raw, u, H, S0)[0], rtol=1e-12, what="bruteforce with state")
+    P.spin_state_alone(lambda r, k, v, w_raw, u, H, S0: (
+        wkv6_bruteforce(r, k, v, w_raw, u, H, "causal", state_in=S0),
+        _ref_state(r, k, v, w_raw, u, H, S0)[1]))
+
+
+def test_state_passing_is_causal_only():
+    r, k, v, w_raw, u = P.draw(1, 3, 8, 2, 5)
+    with pytest.raises(ValueError):
+        wkv6_ref(r, k, v, w_raw, u, 2, "bidirectional", state_in=np.zeros((1, 2, 4, 4)))
+    with pytest.raises(ValueError):
+        wkv6_ref(r, k, v, w_raw, u, 2, "causal", state_in=np.zeros((1, 2, 4, 5)))
+
+
+def _state_mutant(kind):
+    """A copy of the causal recurrence with a state and one planted mistake."""
+
+    def impl(r, k, v, w_raw, u, H, S0):
+        B, T, C = r.shape
+        N = C // H
+        hs = lambda x: np.asarray(x, np.float64).reshape(B, T, H, N).transpose(0, 2, 1, 3)
+        R, K, V, W = hs(r), hs(k), hs(v), np.exp(-np.exp(hs(w_raw)))
+        U = np.asarray(u, np.float64).reshape(H, N)
+        S = np.array(S0, np.float64)
+        if kind == "state_transposed":
+            S = S.transpose(0, 1, 3, 2).copy()
+        if kind == "state_decayed_first" and T > 0:   # S0 decayed by w_0 before token 0 reads it
+            S = W[:, :, 0, :, None] * S
+        Y = np.zeros((B, H, T, N))
+        for t in range(T):
+            kv = K[:, :, t, :, None] * V[:, :, t, None, :]
+            Y[:, :, t] = np.einsum("bhc,bhcn->bhn", R[:, :, t], S + U[None, :, :, None] * kv)
+            if kind == "last_token_not_in_state" and t == T - 1:
+                break
+            S = W[:, :, t, :, None] * S + kv
+        if kind == "state_scaled_twice":
+            S = 2.0 * S - np.array(S0, np.float64) * 0.0 + 0.5 * S
+        return Y.transpose(0, 2, 1, 3).reshape(B, T, C), S
+
+    return impl
+
+
+def test_unmutated_state_copy_holds_state_pins():
+    assert P.violated_state_pins(_state_mutant("none")) == []
+
+
+@pytest.mark.parametrize("kind", ["state_transposed", "state_decayed_first", "last_token_not_in_state",
+                                  "state_scaled_twice"])
+def test_planted_state_mistake_is_caught(kind):
+    assert P.violated_state_pins(_state_mutant(kind)), f"state mutant {kind} passed every pin"
