@@ -1220,6 +1220,103 @@ __global__ __launch_bounds__(NT) void state_copy_kernel(const float* __restrict_
     dst[i] = src ? src[i] : 0.f;
 }
 
+// ---------------------------------------------------------------------------
+// Causal calls of a few tokens (decoding): the recurrence itself, one token
+// after the other, with the state in registers.  One workgroup per
+// (batch, head); thread t holds state rows 4 (t / 16) .. + 3 at columns
+// 4 (t % 16) .. + 3.  Per token: y_t[n] = sum_c r_t[c] S[c][n] + d_t v_t[n]
+// with d_t = sum_c r_t[c] u[c] k_t[c] (partial sums over the thread's rows,
+// combined across the 16 row groups through LDS), then
+// S[c][n] <- w_t[c] S[c][n] + k_t[c] v_t[n].  fp32 throughout.
+constexpr int kDecodeMaxT = 4;
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if constexpr (BF16) {
+    const uint16_t b = static_cast<const uint16_t*>(p)[i];
+    return __uint_as_float((uint32_t)b << 16);
+  } else {
+    return static_cast<const float*>(p)[i];
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(NT) void decode_kernel(Params p) {
+  __shared__ float sPart[NT / 64][HS];   // per wave: partial y over its row groups
+  __shared__ float sBonus;
+  const int bh = blockIdx.x;
+  const int b = bh / p.H, h = bh % p.H;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n0 = 4 * (t & 15), c0 = 4 * (t >> 4);
+  float S[4][4];   // S[i][j] = state row c0 + i, column n0 + j
+  if (p.s_in) {
+    const float* si = p.s_in + (int64_t)bh * PL;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 q = *reinterpret_cast<const float4*>(si + (c0 + i) * HS + n0);
+      S[i][0] = q.x; S[i][1] = q.y; S[i][2] = q.z; S[i][3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i][j] = 0.f;
+  }
+  const float ul = p.u[h * HS + lane];
+  for (int tok = 0; tok < p.T; ++tok) {
+    const int64_t row = ((int64_t)b * p.T + tok) * p.C + (int64_t)h * HS;
+    float r[4], k[4], w[4], v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = load_elem<BF16>(p.r, row + c0 + i);
+      k[i] = load_elem<BF16>(p.k, row + c0 + i);
+      w[i] = ex2(-kLog2e * ex2(load_elem<BF16>(p.w, row + c0 + i) * kLog2e));
+      v[i] = load_elem<BF16>(p.v, row + n0 + i);
+    }
+    // partial y over the thread's four rows, summed over the row groups of
+    // the wave (lanes 16 apart share the columns)
+    float yp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a = fmaf(r[i], S[i][j], a);
+      a += __shfl_xor(a, 16);
+      a += __shfl_xor(a, 32);
+      yp[j] = a;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sPart[wave][n0 + j] = yp[j];
+    }
+    if (wave == 0) {
+      // d = sum_c r[c] u[c] k[c] over the head's 64 channels (lane = c)
+      float d = load_elem<BF16>(p.r, row + lane) * ul * load_elem<BF16>(p.k, row + lane);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) d += __shfl_xor(d, m);
+      if (lane == 0) sBonus = d;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      float y = sBonus * load_elem<BF16>(p.v, row + lane);
+#pragma unroll
+      for (int wv = 0; wv < NT / 64; ++wv) y += sPart[wv][lane];
+      p.y[row + lane] = y;
+    }
+    __syncthreads();   // sPart and sBonus are reused by the next token
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i][j] = fmaf(w[i], S[i][j], k[i] * v[j]);
+  }
+  if (p.s_out) {
+    float* so = p.s_out + (int64_t)bh * PL;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(so + (c0 + i) * HS + n0) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+  }
+}
+
 struct Plan {
   int NC, G, SEGC;
 };
@@ -1285,7 +1382,7 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
 }  // namespace
 
 size_t workspace_bytes(const FwdArgs& a) {
-  if (a.T == 0) return 0;
+  if (a.T == 0 || (!a.bidirectional && a.T <= kDecodeMaxT)) return 0;
   const Plan pl = plan(a);
   if (pl.G == 1) return 0;
   return (size_t)a.B * a.H * pl.G * 2 * kSummFloats * sizeof(float);
@@ -1298,6 +1395,26 @@ hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream) {
     const int64_t nblk = (n + NT - 1) / NT;
     const unsigned grid = (unsigned)(nblk < 1024 ? nblk : 1024);
     hipLaunchKernelGGL(state_copy_kernel, dim3(grid), dim3(NT), 0, stream, a.s_in, a.s_out, n);
+    return hipGetLastError();
+  }
+  if (!a.bidirectional && a.T <= kDecodeMaxT) {
+    Params p{};
+    p.r = a.r;
+    p.k = a.k;
+    p.v = a.v;
+    p.w = a.w_raw;
+    p.u = a.u;
+    p.y = a.y;
+    p.s_in = a.s_in;
+    p.s_out = a.s_out;
+    p.T = a.T;
+    p.C = a.C;
+    p.H = (int)a.H;
+    const dim3 grid((unsigned)(a.B * a.H));
+    if (a.bf16)
+      hipLaunchKernelGGL(decode_kernel<true>, grid, dim3(NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL(decode_kernel<false>, grid, dim3(NT), 0, stream, p);
     return hipGetLastError();
   }
   const Plan pl = plan(a);

@@ -55,7 +55,7 @@ def check(tag, y, S, y_ref, S_ref, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 130, 257])
+@pytest.mark.parametrize("T", [1, 2, 4, 5, 63, 64, 65, 130, 257])
 def test_state_in_out(torch_cuda, T, dtype):
     B, H = 2, 3
     x = I.random_inputs(B, T, 64 * H, H, seed=2000 + T, dtype=dtype, **SLOW)
@@ -179,3 +179,23 @@ def test_state_through_the_slow_path(torch_cuda):
     y, S = run_state(x, H, "f32", S0)
     y_ref, S_ref = ref_state(x, H, S0)
     check("slow path f32", y, S, y_ref, S_ref, "f32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", ["no_decay", "fast_decay", "mixed"])
+def test_few_token_calls_decay_extremes(torch_cuda, case, dtype):
+    """Calls of at most four tokens run the token-by-token kernel; decays at
+    the documented ends (w = 1, w_raw = 1.5) and mixed."""
+    B, H, T = 3, 2, 3
+    x = I.random_inputs(B, T, 64 * H, H, seed=60, dtype=dtype)
+    if case == "no_decay":
+        x["w_raw"][:] = -np.inf
+    elif case == "fast_decay":
+        x["w_raw"][:] = 1.5
+    else:
+        x["w_raw"] = np.random.default_rng(61).choice(
+            np.array([-np.inf, -20.0, -4.0, 0.0, 1.5], np.float32), size=x["w_raw"].shape)
+    S0 = state_of(B, H, 62)
+    y, S = run_state(x, H, dtype, S0)
+    y_ref, S_ref = ref_state(x, H, S0)
+    check(f"few tokens {case} {dtype}", y, S, y_ref, S_ref, dtype)
