@@ -813,8 +813,10 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool have_S = false;
-  // causal calls may start from a given state (the forward sweep only)
-  if (!REV && MODE != kState && p.s_in) {
+  // causal calls may start from a given state (the forward sweep of a causal
+  // call: MODE kOut and not REV; never a bidirectional call)
+  constexpr bool CAUSAL_OUT = !REV && MODE == kOut;
+  if (CAUSAL_OUT && p.s_in) {
     const float* si = p.s_in + (int64_t)bh * PL;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -845,7 +847,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
   float gsum[4] = {0.f, 0.f, 0.f, 0.f};   // kState: total log2 decay of the state rows
   // the sweep that ends at the sequence's last token also updates the state
   // with the last chunk when the caller wants the final state
-  const bool keep_state = !REV && MODE != kState && p.s_out && seg == p.G - 1;
+  const bool keep_state = CAUSAL_OUT && p.s_out && seg == p.G - 1;
 
   // The state entering a chunk goes to sS (pre-split) right after the chunk's
   // first barrier: every wave has then finished the previous chunk's phase C,
