@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define WKV6_ABI_VERSION 2
+#define WKV6_ABI_VERSION 3
 
 /* mode */
 #define WKV6_MODE_CAUSAL        0
@@ -139,6 +139,33 @@ int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H,
                    const void* r, const void* k, const void* v, const void* w_raw,
                    const float* u, float* y, const float* s_in, float* s_out,
                    int dtype, void* stream);
+
+/*
+ * wkv6_bwd -- gradients of L = sum(y * dy) for y = the wkv6_fwd result, for
+ * training.  The pages' CUDA extension has a backward kernel next to the
+ * forward one that returns the gradients of all five inputs (CUDA-kernels
+ * page of deepglint/rwkv-clip, section "Backward Pass Gradient
+ * Computation"); the steps here are derived from the recurrence above.
+ *
+ *   r, k, v, w_raw, u, B, T, C, H, mode, dtype
+ *           as for wkv6_fwd (same layouts and types).
+ *   dy      device pointer to the float32 [B, T, C] gradient of y.
+ *   dr, dk, dv, dw_raw
+ *           device pointers to float32 [B, T, C] outputs (always float32,
+ *           whatever dtype): dL/dr, dL/dk, dL/dv and dL/dw_raw (the
+ *           derivative through w = exp(-exp(w_raw))).  Fully overwritten.
+ *   du      device pointer to a float32 [C] output: dL/du summed over the
+ *           batch and the tokens.  T == 0 sets it to zero.
+ *
+ * B == 0 is a no-op.  The outputs must not overlap one another or any input
+ * (INVALID_ARG).  The call takes a stream-ordered workspace (B*C*4 bytes,
+ * plus B*T*C*4 in bidirectional mode) and runs two token-by-token passes per
+ * (batch, head) in float32; errors otherwise as for wkv6_fwd.
+ */
+int wkv6_bwd(int64_t B, int64_t T, int64_t C, int64_t H,
+             const void* r, const void* k, const void* v, const void* w_raw,
+             const float* u, const float* dy, float* dr, float* dk, float* dv,
+             float* dw_raw, float* du, int mode, int dtype, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* wkv6_status_str(int status);

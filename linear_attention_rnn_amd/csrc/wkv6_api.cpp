@@ -43,12 +43,12 @@ int check_sizes(int64_t B, int64_t T, int64_t C, int64_t H, int mode, int dtype)
   return WKV6_OK;
 }
 
-// Pointer checks for a call with B, T > 0: present, aligned, y clear of the
-// inputs.
+// Pointer checks for a call with B, T > 0: present, aligned, and the [B,T,C]
+// float32 tensor y (named yname) clear of the inputs.
 int check_tensors(int64_t B, int64_t T, int64_t C, int dtype, const void* r, const void* k, const void* v,
-                  const void* w_raw, const float* u, const float* y) {
+                  const void* w_raw, const float* u, const float* y, const char* yname = "y") {
   const void* ptrs[6] = {r, k, v, w_raw, u, y};
-  const char* names[6] = {"r", "k", "v", "w_raw", "u", "y"};
+  const char* names[6] = {"r", "k", "v", "w_raw", "u", yname};
   for (int i = 0; i < 6; ++i) {
     if (!ptrs[i]) return fail(WKV6_ERR_INVALID_ARG, std::string("null pointer: ") + names[i]);
   }
@@ -61,9 +61,9 @@ int check_tensors(int64_t B, int64_t T, int64_t C, int dtype, const void* r, con
   const size_t ybytes = elems * 4;
   for (int i = 0; i < 4; ++i) {
     if (overlaps(y, ybytes, ptrs[i], elems * isz))
-      return fail(WKV6_ERR_INVALID_ARG, std::string("y overlaps ") + names[i]);
+      return fail(WKV6_ERR_INVALID_ARG, std::string(yname) + " overlaps " + names[i]);
   }
-  if (overlaps(y, ybytes, u, (size_t)C * 4)) return fail(WKV6_ERR_INVALID_ARG, "y overlaps u");
+  if (overlaps(y, ybytes, u, (size_t)C * 4)) return fail(WKV6_ERR_INVALID_ARG, std::string(yname) + " overlaps u");
   return WKV6_OK;
 }
 
@@ -168,6 +168,73 @@ int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, co
   a.s_in = s_in;
   a.s_out = s_out;
   return run(a, static_cast<hipStream_t>(stream));
+}
+
+int wkv6_bwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k, const void* v,
+             const void* w_raw, const float* u, const float* dy, float* dr, float* dk, float* dv,
+             float* dw_raw, float* du, int mode, int dtype, void* stream) {
+  g_last_error.clear();
+  int st = check_sizes(B, T, C, H, mode, dtype);
+  if (st != WKV6_OK || B == 0) return st;
+  if (!du) return fail(WKV6_ERR_INVALID_ARG, "null pointer: du");
+  if (reinterpret_cast<uintptr_t>(du) % 16) return fail(WKV6_ERR_MISALIGNED, "pointer not 16-byte aligned: du");
+  if (T > 0) {
+    if ((st = check_tensors(B, T, C, dtype, r, k, v, w_raw, u, dy, "dy")) != WKV6_OK) return st;
+    const size_t elems = (size_t)B * (size_t)T * (size_t)C;
+    const size_t isz = dtype == WKV6_DTYPE_BF16 ? 2 : 4;
+    const void* outs[4] = {dr, dk, dv, dw_raw};
+    const char* onames[4] = {"dr", "dk", "dv", "dw_raw"};
+    const void* ins[6] = {r, k, v, w_raw, dy, u};
+    const size_t inb[6] = {elems * isz, elems * isz, elems * isz, elems * isz, elems * 4, (size_t)C * 4};
+    const char* inames[6] = {"r", "k", "v", "w_raw", "dy", "u"};
+    for (int i = 0; i < 4; ++i) {
+      if (!outs[i]) return fail(WKV6_ERR_INVALID_ARG, std::string("null pointer: ") + onames[i]);
+      if (reinterpret_cast<uintptr_t>(outs[i]) % 16)
+        return fail(WKV6_ERR_MISALIGNED, std::string("pointer not 16-byte aligned: ") + onames[i]);
+      for (int j = 0; j < 6; ++j) {
+        if (overlaps(outs[i], elems * 4, ins[j], inb[j]))
+          return fail(WKV6_ERR_INVALID_ARG, std::string(onames[i]) + " overlaps " + inames[j]);
+      }
+      for (int j = 0; j < i; ++j) {
+        if (overlaps(outs[i], elems * 4, outs[j], elems * 4))
+          return fail(WKV6_ERR_INVALID_ARG, std::string(onames[i]) + " overlaps " + onames[j]);
+      }
+      if (overlaps(outs[i], elems * 4, du, (size_t)C * 4))
+        return fail(WKV6_ERR_INVALID_ARG, std::string(onames[i]) + " overlaps du");
+    }
+    for (int j = 0; j < 6; ++j) {
+      if (overlaps(du, (size_t)C * 4, ins[j], inb[j]))
+        return fail(WKV6_ERR_INVALID_ARG, std::string("du overlaps ") + inames[j]);
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  wkv6::BwdArgs a;
+  a.B = B;
+  a.T = T;
+  a.C = C;
+  a.H = H;
+  a.r = r;
+  a.k = k;
+  a.v = v;
+  a.w_raw = w_raw;
+  a.u = u;
+  a.dy = dy;
+  a.dr = dr;
+  a.dk = dk;
+  a.dv = dv;
+  a.dw_raw = dw_raw;
+  a.du = du;
+  a.bidirectional = mode == WKV6_MODE_BIDIRECTIONAL;
+  a.bf16 = dtype == WKV6_DTYPE_BF16;
+  void* ws = nullptr;
+  const size_t ws_bytes = wkv6::bwd_workspace_bytes(a);
+  hipError_t e = ws_bytes ? hipMallocAsync(&ws, ws_bytes, s) : hipSuccess;
+  if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("workspace allocation: ") + hipGetErrorString(e));
+  e = wkv6::enqueue_bwd(a, ws, s);
+  const hipError_t ef = ws ? hipFreeAsync(ws, s) : hipSuccess;
+  if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  if (ef != hipSuccess) return fail(WKV6_ERR_HIP, std::string("workspace release: ") + hipGetErrorString(ef));
+  return WKV6_OK;
 }
 
 }  // extern "C"

@@ -33,4 +33,25 @@ size_t workspace_bytes(const FwdArgs& a);
 // Returns the first HIP error, if any.
 hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream);
 
+struct BwdArgs {
+  int64_t B, T, C, H;
+  const void* r;
+  const void* k;
+  const void* v;
+  const void* w_raw;
+  const float* u;
+  const float* dy;   // [B, T, C] float32
+  float* dr;         // [B, T, C] float32 outputs
+  float* dk;
+  float* dv;
+  float* dw_raw;
+  float* du;         // [C]
+  bool bidirectional;
+  bool bf16;
+};
+
+// Workspace of a backward call (always > 0) and its kernels (wkv6_backward.hip).
+size_t bwd_workspace_bytes(const BwdArgs& a);
+hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
+
 }  // namespace wkv6

@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
         L.wkv6_fwd_state.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                      ctypes.c_int, vp]
         L.wkv6_fwd_state.restype = ctypes.c_int
+        L.wkv6_bwd.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                               ctypes.c_int, ctypes.c_int, vp]
+        L.wkv6_bwd.restype = ctypes.c_int
         L.wkv6_status_str.argtypes = [ctypes.c_int]
         L.wkv6_status_str.restype = ctypes.c_char_p
         L.wkv6_last_error.argtypes = []
@@ -179,3 +182,32 @@ def fwd(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
     if st != OK:
         raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
     return out
+
+
+def bwd_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, u: int, dy: int,
+            dr: int, dk: int, dv: int, dw_raw: int, du: int, mode: int, dtype: int, stream: int = 0) -> int:
+    """Direct call of wkv6_bwd with integer addresses."""
+    return lib().wkv6_bwd(B, T, C, H, r, k, v, w_raw, u, dy, dr, dk, dv, dw_raw, du, mode, dtype, stream)
+
+
+def bwd(r, k, v, w_raw, u, dy, H: int, mode: str = "causal", stream=None) -> dict:
+    """Gradients of sum(y * dy) for y = fwd(r, k, v, w_raw, u, H, mode).
+
+    dy: contiguous float32 CUDA tensor [B, T, C].  Returns a dict of float32
+    tensors: "r", "k", "v", "w_raw" ([B, T, C]) and "u" ([C]).
+    """
+    import torch
+
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    B, T, C, dtype = _check_inputs(r, k, v, w_raw, u)
+    if dy.shape != (B, T, C) or dy.dtype != torch.float32 or not dy.is_cuda or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous float32 GPU tensor [B, T, C]")
+    g = {name: torch.empty((B, T, C), dtype=torch.float32, device=r.device) for name in ("r", "k", "v", "w_raw")}
+    g["u"] = torch.empty((C,), dtype=torch.float32, device=r.device)
+    st = bwd_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(), u.data_ptr(),
+                 dy.data_ptr(), g["r"].data_ptr(), g["k"].data_ptr(), g["v"].data_ptr(), g["w_raw"].data_ptr(),
+                 g["u"].data_ptr(), _MODES[mode], dtype, _stream_handle(stream, r.device))
+    if st != OK:
+        raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
+    return g

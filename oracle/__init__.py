@@ -10,12 +10,14 @@ Contents (all arithmetic in float64 on the exact input values):
 * ``wkv6_ref``         -- the recurrent definition, one token at a time;
 * ``wkv6_bruteforce``  -- the explicit double sum over token pairs, with every
                           decay product formed term by term (tiny inputs only);
-* ``decay``            -- w = exp(-exp(w_raw)).
+* ``decay``            -- w = exp(-exp(w_raw));
+* ``wkv6_ref_backward`` -- gradients of sum(y * dy) w.r.t. every input, by the
+                          adjoint of the recurrence.
 
 Every function here is pinned by tests that do not rely on the oracle itself
 (closed forms, a hand-worked example, invariants, brute force on tiny inputs);
 there is no "parity unpinned" function in this package.
 """
-from .wkv6_oracle import decay, wkv6_ref, wkv6_bruteforce, split_heads, merge_heads
+from .wkv6_oracle import decay, wkv6_ref, wkv6_bruteforce, wkv6_ref_backward, split_heads, merge_heads
 
-__all__ = ["decay", "wkv6_ref", "wkv6_bruteforce", "split_heads", "merge_heads"]
+__all__ = ["decay", "wkv6_ref", "wkv6_bruteforce", "wkv6_ref_backward", "split_heads", "merge_heads"]

@@ -162,3 +162,70 @@ def wkv6_bruteforce(r, k, v, w_raw, u, H: int, mode: str = "causal", state_in=No
                 g = g * W[:, :, j, :]
             Y[:, :, t, :] += np.einsum("bhc,bhc,bhcn->bhn", R[:, :, t, :], g, S0)
     return merge_heads(Y)
+
+
+def _causal_backward(R, K, V, W, WR, U, DY, use_u: bool):
+    """Adjoint of the causal recurrence for one direction, arrays [B, H, T, N]
+    (float64).  Returns dR, dK, dV, dWR (gradient w.r.t. w_raw) and dU [H, N].
+
+    With S_t the state after token t and G_t = dL/dS_t:
+      dr_t[c] = sum_n dy_t[n] (S_{t-1}[c, n] + u[c] k_t[c] v_t[n])
+      G_{t-1} = w_t[c] G_t[c, n] + r_t[c] dy_t[n]          (G_{T-1} = 0)
+      dk_t[c] = sum_n G_t[c, n] v_t[n] + r_t[c] u[c] (dy_t . v_t)
+      dv_t[n] = sum_c G_t[c, n] k_t[c] + (sum_c r_t[c] u[c] k_t[c]) dy_t[n]
+      dw_t[c] = sum_n G_t[c, n] S_{t-1}[c, n]
+    and w = exp(-exp(w_raw)) gives dw_raw = dw * w * (-exp(w_raw))."""
+    B, H, T, N = R.shape
+    Uu = U[None] if use_u else np.zeros_like(U)[None]
+    S = np.zeros((B, H, N, N))
+    states = np.zeros((B, H, T, N, N))          # S_{t-1} for every t
+    dR = np.zeros_like(R)
+    for t in range(T):
+        states[:, :, t] = S
+        dyv = (DY[:, :, t] * V[:, :, t]).sum(-1)                      # [B, H]
+        dR[:, :, t] = np.einsum("bhcn,bhn->bhc", S, DY[:, :, t]) + Uu * K[:, :, t] * dyv[..., None]
+        S = W[:, :, t, :, None] * S + K[:, :, t, :, None] * V[:, :, t, None, :]
+    G = np.zeros((B, H, N, N))
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    dW = np.zeros_like(W)
+    dU = np.zeros((H, N))
+    for t in range(T - 1, -1, -1):
+        dyv = (DY[:, :, t] * V[:, :, t]).sum(-1)
+        ruk = (R[:, :, t] * Uu * K[:, :, t]).sum(-1)                   # [B, H]
+        dK[:, :, t] = np.einsum("bhcn,bhn->bhc", G, V[:, :, t]) + R[:, :, t] * Uu * dyv[..., None]
+        dV[:, :, t] = np.einsum("bhcn,bhc->bhn", G, K[:, :, t]) + ruk[..., None] * DY[:, :, t]
+        dW[:, :, t] = np.einsum("bhcn,bhcn->bhc", G, states[:, :, t])
+        if use_u:
+            dU += (R[:, :, t] * K[:, :, t] * dyv[..., None]).sum(0)
+        G = W[:, :, t, :, None] * G + R[:, :, t, :, None] * DY[:, :, t, None, :]
+    dWR = dW * W * (-np.exp(WR))
+    return dR, dK, dV, dWR, dU
+
+
+def wkv6_ref_backward(r, k, v, w_raw, u, dy, H: int, mode: str = "causal") -> dict:
+    """Gradients of L = sum(y * dy) with respect to r, k, v, w_raw and u, for
+    y = wkv6_ref(r, k, v, w_raw, u, H, mode); float64, by the adjoint of the
+    recurrence (the pages' CUDA kernel has a backward kernel alongside the
+    forward one, CUDA-kernels page, section "Backward Pass Gradient
+    Computation"; its steps are not given, so this is derived here).
+
+    Returns {"r", "k", "v", "w_raw": [B, T, C], "u": [C]}.  Bidirectional mode
+    adds the gradients of the later-token sum: the causal adjoint of the
+    time-reversed sequence without the u term.
+    """
+    bidir = _check_mode(mode)
+    R, K, V, WR, DY = (split_heads(x, H) for x in (r, k, v, w_raw, dy))
+    W = np.exp(-np.exp(WR))
+    B, Hh, T, N = R.shape
+    U = np.asarray(u, dtype=np.float64).reshape(Hh, N)
+    dR, dK, dV, dWR, dU = _causal_backward(R, K, V, W, WR, U, DY, True)
+    if bidir:
+        rev = lambda X: X[:, :, ::-1]
+        eR, eK, eV, eWR, _ = _causal_backward(rev(R), rev(K), rev(V), rev(W), rev(WR), U, rev(DY), False)
+        dR += rev(eR)
+        dK += rev(eK)
+        dV += rev(eV)
+        dWR += rev(eWR)
+    return {"r": merge_heads(dR), "k": merge_heads(dK), "v": merge_heads(dV), "w_raw": merge_heads(dWR),
+            "u": dU.reshape(-1)}

@@ -18,8 +18,8 @@ A = 0x10000  # fake, 16-byte aligned addresses: never dereferenced by these call
 
 def test_exports_every_declared_function():
     names = wkv6.header_functions()
-    assert set(names) == {"wkv6_fwd", "wkv6_fwd_state", "wkv6_status_str", "wkv6_last_error",
-                          "wkv6_abi_version"}
+    assert set(names) == {"wkv6_fwd", "wkv6_fwd_state", "wkv6_bwd", "wkv6_status_str",
+                          "wkv6_last_error", "wkv6_abi_version"}
     L = wkv6.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert wkv6.abi_version() == 2
+    assert wkv6.abi_version() == 3
     assert wkv6.status_str(0) == "ok"
     texts = {wkv6.status_str(s) for s in range(5)}
     assert len(texts) == 5
@@ -124,3 +124,45 @@ def test_state_call_empty_batch_is_a_noop():
     assert _call_state(B=0, ptrs=[0] * 6, s_in=0, s_out=0) == wkv6.OK
     assert _call_state(T=0, ptrs=[0] * 6, s_in=0, s_out=0) == wkv6.OK   # nothing to copy
     assert wkv6.last_error() == ""
+
+
+# ---- wkv6_bwd: the same size checks; outputs clear of the inputs and of each other
+def _call_bwd(B=2, T=8, C=128, H=2, ptrs=None, mode=0, dtype=0):
+    p = ptrs or [A + 0x100000 * i for i in range(11)]
+    return wkv6.bwd_raw(B, T, C, H, *p, mode, dtype, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), wkv6.ERR_INVALID_ARG),
+    (dict(mode=3), wkv6.ERR_INVALID_ARG),
+    (dict(C=96, H=2), wkv6.ERR_UNSUPPORTED),
+    (dict(T=2 ** 31), wkv6.ERR_UNSUPPORTED),
+])
+def test_bwd_rejects_bad_sizes(kw, status):
+    assert _call_bwd(**kw) == status
+
+
+@pytest.mark.parametrize("which", range(11))
+def test_bwd_null_pointer(which):
+    p = [A + 0x100000 * i for i in range(11)]
+    p[which] = 0
+    assert _call_bwd(ptrs=p) == wkv6.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which", range(11))
+def test_bwd_misaligned_pointer(which):
+    p = [A + 0x100000 * i for i in range(11)]
+    p[which] += 8
+    assert _call_bwd(ptrs=p) == wkv6.ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("out,other", [(6, 0), (7, 5), (8, 9), (9, 6), (10, 2), (6, 10)])
+def test_bwd_overlapping_output(out, other):
+    p = [A + 0x100000 * i for i in range(11)]
+    p[out] = p[other] + 16
+    assert _call_bwd(ptrs=p) == wkv6.ERR_INVALID_ARG
+    assert "overlaps" in wkv6.last_error()
+
+
+def test_bwd_empty_batch_is_a_noop():
+    assert _call_bwd(B=0, ptrs=[0] * 11) == wkv6.OK

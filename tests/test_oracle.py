@@ -199,3 +199,117 @@ def test_unmutated_state_copy_holds_state_pins():
                                   "state_scaled_twice"])
 def test_planted_state_mistake_is_caught(kind):
     assert P.violated_state_pins(_state_mutant(kind)), f"state mutant {kind} passed every pin"
+
+
+# ------------------------------------------------------------------ backward
+
+def _fd_grad(fn, args, name, eps=1e-6):
+    """Central differences of fn(**args) with respect to args[name]."""
+    x = args[name]
+    g = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape):
+        a = dict(args)
+        xp = x.copy()
+        xp[idx] += eps
+        a[name] = xp
+        fp = fn(**a)
+        xm = x.copy()
+        xm[idx] -= eps
+        a[name] = xm
+        g[idx] = (fp - fn(**a)) / (2 * eps)
+    return g
+
+
+@pytest.mark.parametrize("mode", ["causal", "bidirectional"])
+@pytest.mark.parametrize("shape", [(1, 1, 4, 1), (2, 5, 8, 2), (1, 7, 4, 1)])
+def test_backward_matches_finite_differences(mode, shape):
+    """The gradients of sum(y * dy) agree with central differences of the
+    (pinned) forward oracle: a check that does not use the backward's own
+    recurrences."""
+    from oracle import wkv6_ref_backward
+
+    B, T, C, H = shape
+    r, k, v, w_raw, u = P.draw(B, T, C, H, 600 + T + C)
+    dy = np.random.default_rng(700 + T).normal(size=(B, T, C))
+    g = wkv6_ref_backward(r, k, v, w_raw, u, dy, H, mode)
+    loss = lambda r, k, v, w_raw, u: float((wkv6_ref(r, k, v, w_raw, u, H, mode) * dy).sum())
+    args = {"r": r, "k": k, "v": v, "w_raw": w_raw, "u": u}
+    for name in args:
+        P.close(g[name], _fd_grad(loss, args, name), rtol=1e-7, what=f"d{name} {mode} {shape}")
+
+
+def test_backward_decay_identity():
+    """The decay gradient by the pair-counting identity the GPU kernel uses,
+    dlambda_j = sum_{t>j} r dr - sum_{i>=j} k dk + r_j u k_j (dy_j . v_j) and
+    dw_raw = dlambda * (-exp(w_raw)), equals the oracle's (which takes
+    sum_n G_t S_{t-1} from the states instead)."""
+    from oracle import wkv6_ref_backward
+
+    B, T, C, H = 2, 9, 8, 2
+    r, k, v, w_raw, u = P.draw(B, T, C, H, 620)
+    dy = np.random.default_rng(621).normal(size=(B, T, C))
+    g = wkv6_ref_backward(r, k, v, w_raw, u, dy, H, "causal")
+    rdr, kdk = r * g["r"], k * g["k"]
+    dyv = (P.heads(dy, H) * P.heads(v, H)).sum(-1, keepdims=True)          # [B, T, H, 1]
+    bonus = (P.heads(r, H) * u.reshape(H, C // H) * P.heads(k, H) * dyv).reshape(B, T, C)
+    after = np.cumsum(rdr[:, ::-1], axis=1)[:, ::-1] - rdr                   # sum over t > j
+    from_j = np.cumsum(kdk[:, ::-1], axis=1)[:, ::-1]                       # sum over i >= j
+    dlam = after - from_j + bonus
+    P.close(dlam * -np.exp(w_raw), g["w_raw"], rtol=1e-12, what="decay identity")
+
+
+def _bwd_mutant(kind):
+    """A copy of the causal adjoint with one planted mistake (dr, dk, dv, dW)."""
+
+    def impl(r, k, v, w_raw, u, dy, H):
+        B, T, C = r.shape
+        N = C // H
+        hs = lambda x: np.asarray(x, np.float64).reshape(B, T, H, N).transpose(0, 2, 1, 3)
+        R, K, V, WR, DY = (hs(x) for x in (r, k, v, w_raw, dy))
+        W = np.exp(-np.exp(WR))
+        U = np.asarray(u, np.float64).reshape(H, N)[None]
+        S = np.zeros((B, H, N, N))
+        St = np.zeros((B, H, T, N, N))
+        dR = np.zeros_like(R)
+        for t in range(T):
+            St[:, :, t] = S
+            dyv = (DY[:, :, t] * V[:, :, t]).sum(-1)[..., None]
+            bon = 0.0 if kind == "dr_no_bonus" else U * K[:, :, t] * dyv
+            dR[:, :, t] = np.einsum("bhcn,bhn->bhc", S, DY[:, :, t]) + bon
+            S = W[:, :, t, :, None] * S + K[:, :, t, :, None] * V[:, :, t, None, :]
+        G = np.zeros_like(S)
+        dK, dV, dW = np.zeros_like(K), np.zeros_like(V), np.zeros_like(W)
+        for t in range(T - 1, -1, -1):
+            if kind == "adjoint_updated_first":
+                G = W[:, :, t, :, None] * G + R[:, :, t, :, None] * DY[:, :, t, None, :]
+            dyv = (DY[:, :, t] * V[:, :, t]).sum(-1)[..., None]
+            ruk = (R[:, :, t] * U * K[:, :, t]).sum(-1)[..., None]
+            dK[:, :, t] = np.einsum("bhcn,bhn->bhc", G, V[:, :, t]) + R[:, :, t] * U * dyv
+            Gv = G.transpose(0, 1, 3, 2) if kind == "dv_transposed" else G
+            dV[:, :, t] = np.einsum("bhcn,bhc->bhn", Gv, K[:, :, t]) + ruk * DY[:, :, t]
+            Sprev = S if kind == "dw_current_state" else St[:, :, t]
+            dW[:, :, t] = np.einsum("bhcn,bhcn->bhc", G, Sprev)
+            if kind != "adjoint_updated_first":
+                G = W[:, :, t, :, None] * G + R[:, :, t, :, None] * DY[:, :, t, None, :]
+        back = lambda X: X.transpose(0, 2, 1, 3).reshape(B, T, C)
+        return {"r": back(dR), "k": back(dK), "v": back(dV), "w_raw": back(dW * W * -np.exp(WR))}
+
+    return impl
+
+
+@pytest.mark.parametrize("kind", ["dr_no_bonus", "adjoint_updated_first", "dv_transposed", "dw_current_state"])
+def test_backward_mutant_fails_finite_differences(kind):
+    B, T, C, H = 1, 5, 4, 1
+    r, k, v, w_raw, u = P.draw(B, T, C, H, 640)
+    dy = np.random.default_rng(641).normal(size=(B, T, C))
+    g = _bwd_mutant(kind)(r, k, v, w_raw, u, dy, H)
+    good = _bwd_mutant("none")(r, k, v, w_raw, u, dy, H)
+    loss = lambda r, k, v, w_raw, u: float((wkv6_ref(r, k, v, w_raw, u, H, "causal") * dy).sum())
+    args = {"r": r, "k": k, "v": v, "w_raw": w_raw, "u": u}
+    bad = []
+    for name in ("r", "k", "v", "w_raw"):
+        fd = _fd_grad(loss, args, name)
+        P.close(good[name], fd, rtol=1e-7, what="unmutated copy")
+        if np.max(np.abs(g[name] - fd)) > 1e-6 * max(1.0, np.max(np.abs(fd))):
+            bad.append(name)
+    assert bad, f"backward mutant {kind} passed the finite-difference check"
