@@ -67,200 +67,386 @@ struct BwdParams {
   int H;
 };
 
+// Four consecutive channels of one input row, widened to float32.
 template <bool BF16>
-__device__ __forceinline__ float4 load4(const void* p, int64_t i) {
-  if constexpr (BF16) {
-    const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
-    return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u),
-                       __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xFFFF0000u));
-  } else {
+struct Raw4 {
+  using type = float4;
+};
+template <>
+struct Raw4<true> {
+  using type = uint2;
+};
+
+template <bool BF16>
+__device__ __forceinline__ typename Raw4<BF16>::type ld4(const void* p, int64_t i) {
+  if constexpr (BF16)
+    return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+  else
     return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-  }
+}
+
+__device__ __forceinline__ float4 widen(float4 x) { return x; }
+__device__ __forceinline__ float4 widen(uint2 q) {
+  return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u), __uint_as_float(q.y << 16),
+                     __uint_as_float(q.y & 0xFFFF0000u));
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Sum over the 16 lanes of a DPP row (the thread's column groups).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of a DPP row (xor 1 and xor 2 within quads, then the
+// half-row and row mirrors).  Every lane of the row ends with the same bits.
 __device__ __forceinline__ float row_sum(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
   return x;
 }
 
-struct Tok {
-  float r[4], k[4], wr[4], v[4], dy[4];
+// Four sums over the 16 lanes of a DPP row at once, transposed: lanes l and
+// 15 - l trade the halves of the four values they do not keep, lanes l and
+// 7 - l of each half-row the quarters, and the quads finish with xor 2 and
+// xor 1, so each lane ends with the full sum of one of the four values (which
+// one depends only on the lane; the kernel finds it by reducing 0, 1, 2, 3).
+// hi: lane % 16 >= 8, hq: lane % 8 >= 4.
+__device__ __forceinline__ float row_sums4(const float (&x)[4], bool hi, bool hq) {
+  const float y0 = (hi ? x[2] : x[0]) + dpp<0x140>(hi ? x[0] : x[2]);
+  const float y1 = (hi ? x[3] : x[1]) + dpp<0x140>(hi ? x[1] : x[3]);
+  float z = (hq ? y1 : y0) + dpp<0x141>(hq ? y0 : y1);
+  z += dpp<0x4E>(z);
+  z += dpp<0xB1>(z);
+  return z;
+}
+
+// Four sums over the four 16-lane rows of the wave (lanes l, l^16, l^32,
+// l^48) at once, transposed: a swap of two values between partner rows
+// leaves, after one add, the pair sum of the first value in one row of the
+// pair and of the second value in the other; the 16-row swaps pair the rows,
+// the 32-lane swap the halves.  Each lane ends with the full sum of one of
+// the four values (found, like row_sums4's, by reducing 0, 1, 2, 3).
+__device__ __forceinline__ float rows_sums4(const float (&a)[4]) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[0]), __float_as_uint(a[1]), false, false);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[2]), __float_as_uint(a[3]), false, false);
+  const float s01 = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const float s23 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One sum over the four rows of the wave (every lane ends with it).
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float4 f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float4 keep(bool ok, float4 x) {
+  return ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+__device__ __forceinline__ float at(float4 x, int i) { return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w; }
+
+// Tokens are staged through LDS in blocks of TB: the 256 threads load a
+// block with one coalesced access each per array (thread t: token t / 16 of
+// the block, channels 4 (t % 16) .. + 3), one block ahead of its use, and
+// the outputs of a block leave the same way after it has been processed.
+constexpr int TB = 16;
+
+struct Smem {
+  float r[TB][HS], k[TB][HS], w[TB][HS], x[TB][HS], lam[TB][HS], v[TB][HS], dy[TB][HS];
+  float dyv[TB];
+  float oa[TB][HS], ob[TB][HS];        // per token: dr (pass 1); dk and D (pass 2)
+  float ov[TB][NT / 64][HS];          // per token and wave: partial column sums for dv
 };
 
+// One thread's share of a block as loaded from HBM (zeros past the end).
 template <bool BF16>
-__device__ __forceinline__ Tok load_tok(const BwdParams& p, int64_t row, int c0, int n0) {
-  Tok o;
-  const float4 r = load4<BF16>(p.r, row + c0), k = load4<BF16>(p.k, row + c0);
-  const float4 w = load4<BF16>(p.w, row + c0), v = load4<BF16>(p.v, row + n0);
-  const float4 d = *reinterpret_cast<const float4*>(p.dy + row + n0);
-  o.r[0] = r.x; o.r[1] = r.y; o.r[2] = r.z; o.r[3] = r.w;
-  o.k[0] = k.x; o.k[1] = k.y; o.k[2] = k.z; o.k[3] = k.w;
-  o.wr[0] = w.x; o.wr[1] = w.y; o.wr[2] = w.z; o.wr[3] = w.w;
-  o.v[0] = v.x; o.v[1] = v.y; o.v[2] = v.z; o.v[3] = v.w;
-  o.dy[0] = d.x; o.dy[1] = d.y; o.dy[2] = d.z; o.dy[3] = d.w;
-  return o;
-}
+struct Pre {
+  typename Raw4<BF16>::type r, k, w, v;
+  float4 dy, dr;
+};
 
 // REV: the later-token part of a bidirectional call (reversed token order,
 // no u term, outputs accumulated).
 template <bool BF16, bool REV>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
-  __shared__ float sCol[NT / 64][HS];   // per wave: partial column sums
-  __shared__ float sRuk[NT / 64];
+  __shared__ Smem sm;
   const int bh = blockIdx.x;
   const int b = bh / p.H, h = bh % p.H;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int rg = t >> 4, cg = t & 15;
-  const int c0 = 4 * rg, n0 = 4 * cg;
-  const int64_t T = p.T;
-  auto row_of = [&](int64_t q) {   // sweep position q -> element offset of the token's head row
-    const int64_t tok = REV ? T - 1 - q : q;
-    return (b * T + tok) * p.C + (int64_t)h * HS;
+  // token steps: rows c0 .. c0 + 3 and columns n0 .. n0 + 3 of the state
+  const int c0 = 4 * (t >> 4), n0 = 4 * (t & 15);
+  // staging and output: token ts of the block, channels cc .. cc + 3
+  const int ts = t >> 4, cc = 4 * (t & 15);
+  const int64_t T = p.T, C = p.C;
+  const int nblk = (int)((T + TB - 1) / TB);
+  const int64_t head = (int64_t)b * T * C + (int64_t)h * HS;
+  auto row_of = [&](int64_t q) {   // sweep position -> element offset of the token's head row
+    return head + (REV ? T - 1 - q : q) * C;
   };
-  float u[4];
+  // after row_sums4 this lane holds row c0 + ri; after rows_sums4, column n0 + cj
+  const bool hi = (lane & 8) != 0, hq = (lane & 4) != 0;
+  const float idx[4] = {0.f, 1.f, 2.f, 3.f};
+  const int ri = (int)(row_sums4(idx, hi, hq) * (1.f / 16.f) + 0.5f);
+  const int cj = (int)(rows_sums4(idx) * 0.25f + 0.5f);
+  const float u_ri = REV ? 0.f : p.u[h * HS + c0 + ri];
+  float uc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) u[i] = REV ? 0.f : p.u[h * HS + c0 + i];
+  for (int i = 0; i < 4; ++i) uc[i] = REV ? 0.f : p.u[h * HS + cc + i];
   float* drw = REV ? p.dr_tmp : p.dr;   // where pass 1 leaves dr
 
-  // ---- pass 1: forward, state S, dr
-  float S[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) S[i][j] = 0.f;
-  Tok cur = load_tok<BF16>(p, row_of(0), c0, n0);
-  for (int64_t q = 0; q < T; ++q) {
-    const int64_t row = row_of(q);
-    const Tok x = cur;
-    if (q + 1 < T) cur = load_tok<BF16>(p, row_of(q + 1), c0, n0);
-    float dyv = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dyv = fmaf(x.dy[j], x.v[j], dyv);
-    dyv = row_sum(dyv);
-    float dr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a = fmaf(S[i][j], x.dy[j], a);
-      dr[i] = fmaf(u[i] * x.k[i], dyv, row_sum(a));
-    }
-    if (cg == 0) *reinterpret_cast<float4*>(drw + row + c0) = make_float4(dr[0], dr[1], dr[2], dr[3]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float w = ex2(-kLog2e * ex2(x.wr[i] * kLog2e));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[i][j] = fmaf(w, S[i][j], x.k[i] * x.v[j]);
-    }
-  }
-  __syncthreads();   // pass 1's dr rows are visible to the whole workgroup
+  // decay of a staged value: lambda = -exp(w_raw), w = exp(lambda)
+  auto decay = [](float4 wr, float4& lam, float4& w) {
+    lam = make_float4(-ex2(wr.x * kLog2e), -ex2(wr.y * kLog2e), -ex2(wr.z * kLog2e), -ex2(wr.w * kLog2e));
+    w = make_float4(ex2(lam.x * kLog2e), ex2(lam.y * kLog2e), ex2(lam.z * kLog2e), ex2(lam.w * kLog2e));
+  };
+  // Every prefetch reads a valid row: positions past the end repeat the last
+  // token and staging zeroes them, so the loads need no branch (a branch
+  // would make the compiler wait for them at once).
+  auto at_q = [&](int bi) {
+    const int64_t q = (int64_t)bi * TB + ts;
+    return row_of(q < T ? q : T - 1) + cc;
+  };
+  auto stage_dyv = [&](float4 dy, float4 v) {
+    const float d = row_sum(fmaf(dy.x, v.x, fmaf(dy.y, v.y, fmaf(dy.z, v.z, dy.w * v.w))));
+    if (cc == 0) sm.dyv[ts] = d;
+  };
 
-  // ---- pass 2: backward, adjoint G, dk, dv, dw_raw
-  float G[4][4];
+  // ---------------- pass 1: forward sweep, state S, dr
+  {
+    Pre<BF16> x;
+    float4 old_dr;   // REV: the causal part already in p.dr, for the block whose dr leaves next
+    auto load = [&](int bi) {
+      const int64_t o = at_q(bi);
+      x.k = ld4<BF16>(p.k, o);
+      x.w = ld4<BF16>(p.w, o);
+      x.v = ld4<BF16>(p.v, o);
+      x.dy = f4(p.dy + o);
+    };
+    auto out = [&](int bi) {   // dr of block bi: staged partial sums plus u k (dy . v)
+      const int64_t q = (int64_t)bi * TB + ts;
+      if (q >= T) return;
+      const float4 a = f4(&sm.oa[ts][cc]), k = f4(&sm.k[ts][cc]);
+      const float d = sm.dyv[ts];
+      const float4 dr = make_float4(fmaf(uc[0] * k.x, d, a.x), fmaf(uc[1] * k.y, d, a.y), fmaf(uc[2] * k.z, d, a.z),
+                                    fmaf(uc[3] * k.w, d, a.w));
+      const int64_t o = row_of(q) + cc;
+      st4(drw + o, dr);
+      if (REV) st4(p.dr + o, add4(old_dr, dr));
+    };
+    float S[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) G[i][j] = 0.f;
-  // D (running dlambda without the u term), its compensation, and r dr of the
-  // token after the current one
-  float D[4] = {0.f, 0.f, 0.f, 0.f}, Dc[4] = {0.f, 0.f, 0.f, 0.f}, rdr_next[4] = {0.f, 0.f, 0.f, 0.f};
-  float du[4] = {0.f, 0.f, 0.f, 0.f};
-  cur = load_tok<BF16>(p, row_of(T - 1), c0, n0);
-  for (int64_t q = T - 1; q >= 0; --q) {
-    const int64_t row = row_of(q);
-    const Tok x = cur;
-    if (q > 0) cur = load_tok<BF16>(p, row_of(q - 1), c0, n0);
-    const float4 drq = *reinterpret_cast<const float4*>(drw + row + c0);
-    const float dr[4] = {drq.x, drq.y, drq.z, drq.w};
-    float dyv = 0.f;
+      for (int j = 0; j < 4; ++j) S[i][j] = 0.f;
+    load(0);
+    for (int bi = 0; bi < nblk; ++bi) {
+      __syncthreads();   // the previous block's token steps are done with the staging arrays
+      if (bi > 0) out(bi - 1);
+      {
+        const bool ok = (int64_t)bi * TB + ts < T;
+        const float4 k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v)), dy = keep(ok, x.dy);
+        float4 lam, w;
+        decay(widen(x.w), lam, w);
+        st4(&sm.k[ts][cc], k);
+        st4(&sm.w[ts][cc], w);
+        st4(&sm.v[ts][cc], v);
+        st4(&sm.dy[ts][cc], dy);
+        stage_dyv(dy, v);
+      }
+      __syncthreads();
+      if (REV) old_dr = f4(p.dr + at_q(bi));
+      load(bi + 1 < nblk ? bi + 1 : bi);
+      struct Tk {
+        float4 k, w, v, dy;
+      };
+      auto rd = [&](int tt) {
+        Tk e;
+        e.k = f4(&sm.k[tt][c0]);
+        e.w = f4(&sm.w[tt][c0]);
+        e.v = f4(&sm.v[tt][n0]);
+        e.dy = f4(&sm.dy[tt][n0]);
+        return e;
+      };
+      Tk nx = rd(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dyv = fmaf(x.dy[j], x.v[j], dyv);
-    dyv = row_sum(dyv);
-    // dk (rows), the decay gradient and the u gradient
-    float dk[4], dwr[4];
+      for (int tt = 0; tt < TB; ++tt) {
+        const Tk e = nx;
+        if (tt + 1 < TB) nx = rd(tt + 1);   // the next token's operands are in flight during this one
+        float a[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a = 0.f;
+        for (int i = 0; i < 4; ++i)
+          a[i] = fmaf(S[i][0], e.dy.x, fmaf(S[i][1], e.dy.y, fmaf(S[i][2], e.dy.z, S[i][3] * e.dy.w)));
+        sm.oa[tt][c0 + ri] = row_sums4(a, hi, hq);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a = fmaf(G[i][j], x.v[j], a);
-      const float bonus = x.r[i] * u[i] * x.k[i] * dyv;
-      dk[i] = fmaf(x.r[i] * u[i], dyv, row_sum(a));
-      // D += r_{q+1} dr_{q+1} - k_q dk_q, compensated
-      const float term = fmaf(-x.k[i], dk[i], rdr_next[i]) - Dc[i];
-      const float sum = D[i] + term;
-      Dc[i] = (sum - D[i]) - term;
-      D[i] = sum;
-      rdr_next[i] = x.r[i] * dr[i];
-      dwr[i] = (D[i] + bonus) * -ex2(x.wr[i] * kLog2e);
-      du[i] = fmaf(x.r[i] * x.k[i], dyv, du[i]);
-    }
-    // dv (columns): over the thread's rows, the wave's row groups, then the waves
-    float dvp[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float a = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a = fmaf(G[i][j], x.k[i], a);
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      dvp[j] = a;
-    }
-    float ruk = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ruk = fmaf(x.r[i] * u[i], x.k[i], ruk);
-    ruk += __shfl_xor(ruk, 16);
-    ruk += __shfl_xor(ruk, 32);
-    if (lane < 16) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sCol[wave][n0 + j] = dvp[j];
-      if (lane == 0) sRuk[wave] = ruk;
+        for (int i = 0; i < 4; ++i) {
+          const float ki = at(e.k, i), wi = at(e.w, i);
+          S[i][0] = fmaf(wi, S[i][0], ki * e.v.x);
+          S[i][1] = fmaf(wi, S[i][1], ki * e.v.y);
+          S[i][2] = fmaf(wi, S[i][2], ki * e.v.z);
+          S[i][3] = fmaf(wi, S[i][3], ki * e.v.w);
+        }
+      }
     }
     __syncthreads();
-    if (t < 16) {   // row group 0 writes the 64 columns
-      const float rk = sRuk[0] + sRuk[1] + sRuk[2] + sRuk[3];
-      float dv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dv[j] = fmaf(rk, x.dy[j], sCol[0][n0 + j] + sCol[1][n0 + j] + sCol[2][n0 + j] + sCol[3][n0 + j]);
-      float4* o = reinterpret_cast<float4*>(p.dv + row + n0);
-      if (REV) {
-        const float4 a = *o;
-        dv[0] += a.x; dv[1] += a.y; dv[2] += a.z; dv[3] += a.w;
-      }
-      *o = make_float4(dv[0], dv[1], dv[2], dv[3]);
-    }
-    if (cg == 0) {
-      float4* ok = reinterpret_cast<float4*>(p.dk + row + c0);
-      float4* ow = reinterpret_cast<float4*>(p.dw + row + c0);
-      float4 kk = make_float4(dk[0], dk[1], dk[2], dk[3]);
-      float4 ww = make_float4(dwr[0], dwr[1], dwr[2], dwr[3]);
-      if (REV) {
-        const float4 a = *ok, c = *ow;
-        float4* orr = reinterpret_cast<float4*>(p.dr + row + c0);
-        const float4 d = *orr;
-        kk.x += a.x; kk.y += a.y; kk.z += a.z; kk.w += a.w;
-        ww.x += c.x; ww.y += c.y; ww.z += c.z; ww.w += c.w;
-        *orr = make_float4(d.x + dr[0], d.y + dr[1], d.z + dr[2], d.w + dr[3]);
-      }
-      *ok = kk;
-      *ow = ww;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float w = ex2(-kLog2e * ex2(x.wr[i] * kLog2e));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) G[i][j] = fmaf(w, G[i][j], x.r[i] * x.dy[j]);
-    }
-    __syncthreads();   // sCol / sRuk are rewritten by the next token
+    out(nblk - 1);
   }
-  if (!REV && cg == 0)
-    *reinterpret_cast<float4*>(p.du_part + (int64_t)b * p.C + h * HS + c0) = make_float4(du[0], du[1], du[2], du[3]);
+  __syncthreads();   // pass 1's dr rows are written before pass 2 reads them
+
+  // ---------------- pass 2: backward sweep, adjoint G, dk, dv, dw_raw
+  {
+    Pre<BF16> x;
+    float4 old_k, old_v, old_w;   // REV: the causal parts already in the outputs, for the block that leaves next
+    auto load = [&](int bi) {
+      const int64_t o = at_q(bi);
+      x.r = ld4<BF16>(p.r, o);
+      x.k = ld4<BF16>(p.k, o);
+      x.w = ld4<BF16>(p.w, o);
+      x.v = ld4<BF16>(p.v, o);
+      x.dy = f4(p.dy + o);
+      x.dr = f4(drw + o);
+    };
+    auto load_old = [&](int bi) {
+      const int64_t o = at_q(bi);
+      old_k = f4(p.dk + o);
+      old_v = f4(p.dv + o);
+      old_w = f4(p.dw + o);
+    };
+    float du[4] = {0.f, 0.f, 0.f, 0.f};
+    auto out = [&](int bi) {   // dk, dv, dw_raw of block bi
+      const int64_t q = (int64_t)bi * TB + ts;
+      const float4 r = f4(&sm.r[ts][cc]), k = f4(&sm.k[ts][cc]), dy = f4(&sm.dy[ts][cc]);
+      const float d = sm.dyv[ts];
+      const float4 ru = make_float4(r.x * uc[0], r.y * uc[1], r.z * uc[2], r.w * uc[3]);
+      const float ruk = row_sum(fmaf(ru.x, k.x, fmaf(ru.y, k.y, fmaf(ru.z, k.z, ru.w * k.w))));
+      if (q >= T) return;
+      const float4 lam = f4(&sm.lam[ts][cc]), D = f4(&sm.ob[ts][cc]);
+      float4 dk = f4(&sm.oa[ts][cc]);
+      float4 dv = add4(add4(f4(&sm.ov[ts][0][cc]), f4(&sm.ov[ts][1][cc])),
+                       add4(f4(&sm.ov[ts][2][cc]), f4(&sm.ov[ts][3][cc])));
+      dv = make_float4(fmaf(ruk, dy.x, dv.x), fmaf(ruk, dy.y, dv.y), fmaf(ruk, dy.z, dv.z), fmaf(ruk, dy.w, dv.w));
+      float4 dw = make_float4(fmaf(ru.x * k.x, d, D.x) * lam.x, fmaf(ru.y * k.y, d, D.y) * lam.y,
+                              fmaf(ru.z * k.z, d, D.z) * lam.z, fmaf(ru.w * k.w, d, D.w) * lam.w);
+      if (!REV) {
+        du[0] = fmaf(r.x * k.x, d, du[0]);
+        du[1] = fmaf(r.y * k.y, d, du[1]);
+        du[2] = fmaf(r.z * k.z, d, du[2]);
+        du[3] = fmaf(r.w * k.w, d, du[3]);
+      } else {
+        dk = add4(dk, old_k);
+        dv = add4(dv, old_v);
+        dw = add4(dw, old_w);
+      }
+      const int64_t o = row_of(q) + cc;
+      st4(p.dk + o, dk);
+      st4(p.dv + o, dv);
+      st4(p.dw + o, dw);
+    };
+    float G[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) G[i][j] = 0.f;
+    // D (running dlambda without the u term), its compensation, and r dr of
+    // the token after the current one
+    float D = 0.f, Dc = 0.f, rdr_next = 0.f;   // for row c0 + ri
+    load(nblk - 1);
+    for (int bi = nblk - 1; bi >= 0; --bi) {
+      __syncthreads();   // the previous block's token steps are done with the staging arrays
+      if (bi < nblk - 1) out(bi + 1);
+      {
+        const bool ok = (int64_t)bi * TB + ts < T;
+        const float4 r = keep(ok, widen(x.r)), k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v));
+        const float4 dy = keep(ok, x.dy), dr = keep(ok, x.dr);
+        float4 lam, w;
+        decay(widen(x.w), lam, w);
+        st4(&sm.r[ts][cc], r);
+        st4(&sm.k[ts][cc], k);
+        st4(&sm.w[ts][cc], w);
+        st4(&sm.lam[ts][cc], lam);
+        st4(&sm.x[ts][cc], make_float4(r.x * dr.x, r.y * dr.y, r.z * dr.z, r.w * dr.w));
+        st4(&sm.v[ts][cc], v);
+        st4(&sm.dy[ts][cc], dy);
+        stage_dyv(dy, v);
+      }
+      __syncthreads();
+      if (REV) load_old(bi);
+      load(bi > 0 ? bi - 1 : 0);
+      struct Tk {
+        float4 r, k, w, v, dy;
+        float d, ki, rdri, rui;   // dy . v; k, r dr and r u of row c0 + ri
+      };
+      auto rd = [&](int tt) {
+        Tk e;
+        e.r = f4(&sm.r[tt][c0]);
+        e.k = f4(&sm.k[tt][c0]);
+        e.w = f4(&sm.w[tt][c0]);
+        e.v = f4(&sm.v[tt][n0]);
+        e.dy = f4(&sm.dy[tt][n0]);
+        e.d = sm.dyv[tt];
+        e.ki = sm.k[tt][c0 + ri];
+        e.rdri = sm.x[tt][c0 + ri];
+        e.rui = sm.r[tt][c0 + ri] * u_ri;
+        return e;
+      };
+      Tk nx = rd(TB - 1);
+#pragma unroll
+      for (int tt = TB - 1; tt >= 0; --tt) {
+        const Tk e = nx;
+        if (tt > 0) nx = rd(tt - 1);   // the next token's operands are in flight during this one
+        float a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a[i] = fmaf(G[i][0], e.v.x, fmaf(G[i][1], e.v.y, fmaf(G[i][2], e.v.z, G[i][3] * e.v.w)));
+        const float dk = fmaf(e.rui, e.d, row_sums4(a, hi, hq));
+        // D += r_{q+1} dr_{q+1} - k_q dk_q, compensated
+        const float term = fmaf(-e.ki, dk, rdr_next) - Dc;
+        const float sum = D + term;
+        Dc = (sum - D) - term;
+        D = sum;
+        rdr_next = e.rdri;
+        sm.oa[tt][c0 + ri] = dk;
+        sm.ob[tt][c0 + ri] = D;
+        float b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b[j] = fmaf(G[0][j], e.k.x, fmaf(G[1][j], e.k.y, fmaf(G[2][j], e.k.z, G[3][j] * e.k.w)));
+        sm.ov[tt][wave][n0 + cj] = rows_sums4(b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ri_ = at(e.r, i), wi = at(e.w, i);
+          G[i][0] = fmaf(wi, G[i][0], ri_ * e.dy.x);
+          G[i][1] = fmaf(wi, G[i][1], ri_ * e.dy.y);
+          G[i][2] = fmaf(wi, G[i][2], ri_ * e.dy.z);
+          G[i][3] = fmaf(wi, G[i][3], ri_ * e.dy.w);
+        }
+      }
+    }
+    __syncthreads();
+    out(0);
+    if (!REV) {   // du over the threads that share the channels: rows of the wave, then the waves
+#pragma unroll
+      for (int i = 0; i < 4; ++i) du[i] = rows_sum(du[i]);
+      __syncthreads();
+      if (lane < 16) st4(&sm.ov[0][wave][cc], make_float4(du[0], du[1], du[2], du[3]));
+      __syncthreads();
+      if (t < 16) {
+        const float4 s = add4(add4(f4(&sm.ov[0][0][cc]), f4(&sm.ov[0][1][cc])),
+                              add4(f4(&sm.ov[0][2][cc]), f4(&sm.ov[0][3][cc])));
+        st4(p.du_part + (int64_t)b * C + h * HS + cc, s);
+      }
+    }
+  }
 }
 
 // du[c] = sum over batch items of the per-item parts.
