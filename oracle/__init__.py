@@ -12,12 +12,18 @@ Contents (all arithmetic in float64 on the exact input values):
                           decay product formed term by term (tiny inputs only);
 * ``decay``            -- w = exp(-exp(w_raw));
 * ``wkv6_ref_backward`` -- gradients of sum(y * dy) w.r.t. every input, by the
-                          adjoint of the recurrence.
+                          adjoint of the recurrence;
+* ``wkv5_ref``         -- RWKV-5: the same operator with one decay per channel
+                          for every token;
+* ``wkv4_ref``         -- RWKV-4: the normalised per-channel (vector-state)
+                          operator, in its recurrent form.
 
 Every function here is pinned by tests that do not rely on the oracle itself
 (closed forms, a hand-worked example, invariants, brute force on tiny inputs);
 there is no "parity unpinned" function in this package.
 """
 from .wkv6_oracle import decay, wkv6_ref, wkv6_bruteforce, wkv6_ref_backward, split_heads, merge_heads
+from .variants_oracle import wkv4_ref, wkv5_ref
 
-__all__ = ["decay", "wkv6_ref", "wkv6_bruteforce", "wkv6_ref_backward", "split_heads", "merge_heads"]
+__all__ = ["decay", "wkv6_ref", "wkv6_bruteforce", "wkv6_ref_backward", "split_heads", "merge_heads",
+           "wkv4_ref", "wkv5_ref"]
