@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define WKV6_ABI_VERSION 3
+#define WKV6_ABI_VERSION 4
 
 /* mode */
 #define WKV6_MODE_CAUSAL        0
@@ -101,6 +101,56 @@ extern "C" {
 int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H,
              const void* r, const void* k, const void* v, const void* w_raw,
              const float* u, float* y, int mode, int dtype, void* stream);
+
+/*
+ * wkv5_fwd -- the RWKV-5 ("Eagle") operator: the same matrix-state recurrence
+ * and output as wkv6_fwd, with a decay that is a fixed per-channel parameter
+ * instead of a per-token input ("RWKV Architecture" on llms.blog, section
+ * "RWKV-5 Eagle": each head's 64x64 state decays by exp(-w) per step, with w
+ * a learned vector; RWKV-6 made w depend on the token).
+ *
+ *   w_raw   device pointer to C values of `dtype`, laid out [H, 64]: every
+ *           token uses w[c] = exp(-exp(w_raw[c])), i.e. the pages' w is
+ *           exp(w_raw).  Same supported range as wkv6_fwd.
+ *   Every other argument, the workspace, execution and errors: as wkv6_fwd
+ *   (y must not overlap the C values of w_raw either).
+ */
+int wkv5_fwd(int64_t B, int64_t T, int64_t C, int64_t H,
+             const void* r, const void* k, const void* v, const void* w_raw,
+             const float* u, float* y, int mode, int dtype, void* stream);
+
+/*
+ * wkv4_fwd -- the RWKV-4 operator: a normalised weighted average of the
+ * values with one independent recurrence per channel ("RWKV Architecture"
+ * on llms.blog, section "The Fundamental Mathematical Duality", the baseline
+ * WKV formula, and "The Recurrent Inference Formulation"):
+ *
+ *   WKV_t[c] = ( sum_{i<t} e^{-(t-1-i) w[c] + k_i[c]} v_i[c] + e^{u[c] + k_t[c]} v_t[c] )
+ *            / ( sum_{i<t} e^{-(t-1-i) w[c] + k_i[c]}        + e^{u[c] + k_t[c]} )
+ *
+ * Causal only (the pages give no bidirectional form); no heads.
+ *
+ *   B, T, C   batch, tokens, channels (any C >= 0).
+ *   k, v      device pointers to contiguous row-major [B, T, C] tensors of
+ *             `dtype` (WKV6_DTYPE_F32 or WKV6_DTYPE_BF16).
+ *   w         device pointer to C float32 decay rates: every step multiplies
+ *             the history by exp(-w) (the pages take w >= 0; +inf keeps
+ *             only the previous token; -inf and NaN are not supported).
+ *   u         device pointer to C float32 bonuses of the current token.
+ *   y         device pointer to a [B, T, C] float32 output, fully
+ *             overwritten; must not overlap k, v, w or u.
+ *   stream    a hipStream_t passed as void* (NULL = the null stream).
+ *
+ * The kernels keep each channel's numerator and denominator scaled by the
+ * largest exponent seen so far, so any finite keys work in float32.  Long
+ * sequences over few channels are cut into segments; such calls take a
+ * temporary device workspace of 2 * B * segments * 3 * C * 4 bytes,
+ * allocated and released in stream order (hipMallocAsync / hipFreeAsync).
+ * Ownership, execution and errors as wkv6_fwd (status codes, nothing
+ * enqueued on a failed check, values not checked); B, T or C = 0 is a no-op.
+ */
+int wkv4_fwd(int64_t B, int64_t T, int64_t C, const void* k, const void* v,
+             const float* w, const float* u, float* y, int dtype, void* stream);
 
 /*
  * wkv6_fwd_state -- a causal forward that starts from a given state and hands

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libwkv6.so")
-SOURCES = ["wkv6_kernels.hip", "wkv6_backward.hip", "wkv6_api.cpp"]
+SOURCES = ["wkv6_kernels.hip", "wkv6_backward.hip", "wkv4_kernels.hip", "wkv6_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -45,8 +45,10 @@ int check_sizes(int64_t B, int64_t T, int64_t C, int64_t H, int mode, int dtype)
 
 // Pointer checks for a call with B, T > 0: present, aligned, and the [B,T,C]
 // float32 tensor y (named yname) clear of the inputs.
+// w_static: w_raw holds C values (one decay for every token) instead of B*T*C.
 int check_tensors(int64_t B, int64_t T, int64_t C, int dtype, const void* r, const void* k, const void* v,
-                  const void* w_raw, const float* u, const float* y, const char* yname = "y") {
+                  const void* w_raw, const float* u, const float* y, const char* yname = "y",
+                  bool w_static = false) {
   const void* ptrs[6] = {r, k, v, w_raw, u, y};
   const char* names[6] = {"r", "k", "v", "w_raw", "u", yname};
   for (int i = 0; i < 6; ++i) {
@@ -60,7 +62,8 @@ int check_tensors(int64_t B, int64_t T, int64_t C, int dtype, const void* r, con
   const size_t isz = dtype == WKV6_DTYPE_BF16 ? 2 : 4;
   const size_t ybytes = elems * 4;
   for (int i = 0; i < 4; ++i) {
-    if (overlaps(y, ybytes, ptrs[i], elems * isz))
+    const size_t n = (i == 3 && w_static) ? (size_t)C : elems;
+    if (overlaps(y, ybytes, ptrs[i], n * isz))
       return fail(WKV6_ERR_INVALID_ARG, std::string(yname) + " overlaps " + names[i]);
   }
   if (overlaps(y, ybytes, u, (size_t)C * 4)) return fail(WKV6_ERR_INVALID_ARG, std::string(yname) + " overlaps u");
@@ -135,6 +138,18 @@ int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const vo
   return run(make_args(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype), static_cast<hipStream_t>(stream));
 }
 
+int wkv5_fwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k,
+             const void* v, const void* w_raw, const float* u, float* y, int mode, int dtype,
+             void* stream) {
+  g_last_error.clear();
+  int st = check_sizes(B, T, C, H, mode, dtype);
+  if (st != WKV6_OK || B == 0 || T == 0) return st;
+  if ((st = check_tensors(B, T, C, dtype, r, k, v, w_raw, u, y, "y", true)) != WKV6_OK) return st;
+  wkv6::FwdArgs a = make_args(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype);
+  a.w_static = true;
+  return run(a, static_cast<hipStream_t>(stream));
+}
+
 int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k,
                    const void* v, const void* w_raw, const float* u, float* y, const float* s_in,
                    float* s_out, int dtype, void* stream) {
@@ -168,6 +183,53 @@ int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, co
   a.s_in = s_in;
   a.s_out = s_out;
   return run(a, static_cast<hipStream_t>(stream));
+}
+
+int wkv4_fwd(int64_t B, int64_t T, int64_t C, const void* k, const void* v, const float* w, const float* u,
+             float* y, int dtype, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || T < 0 || C < 0) return fail(WKV6_ERR_INVALID_ARG, "sizes must be B, T, C >= 0");
+  if (dtype != WKV6_DTYPE_F32 && dtype != WKV6_DTYPE_BF16) return fail(WKV6_ERR_INVALID_ARG, "unknown dtype");
+  if (B == 0 || T == 0 || C == 0) return WKV6_OK;
+  // grid: batch items x segments in x (at most B * T / 64 + B), 256-channel blocks in y
+  if (B > INT_MAX / 2 || T > INT64_MAX / B / C || (C + 255) / 256 > 65535 || B * ((T + 63) / 64 + 1) > INT_MAX)
+    return fail(WKV6_ERR_UNSUPPORTED, "sizes exceed the supported index range");
+  const void* ptrs[5] = {k, v, w, u, y};
+  const char* names[5] = {"k", "v", "w", "u", "y"};
+  for (int i = 0; i < 5; ++i)
+    if (!ptrs[i]) return fail(WKV6_ERR_INVALID_ARG, std::string("null pointer: ") + names[i]);
+  for (int i = 0; i < 5; ++i)
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16)
+      return fail(WKV6_ERR_MISALIGNED, std::string("pointer not 16-byte aligned: ") + names[i]);
+  const size_t elems = (size_t)B * (size_t)T * (size_t)C, isz = dtype == WKV6_DTYPE_BF16 ? 2 : 4;
+  const size_t nb[4] = {elems * isz, elems * isz, (size_t)C * 4, (size_t)C * 4};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(y, elems * 4, ptrs[i], nb[i])) return fail(WKV6_ERR_INVALID_ARG, std::string("y overlaps ") + names[i]);
+  wkv6::Wkv4Args a;
+  a.B = B;
+  a.T = T;
+  a.C = C;
+  a.k = k;
+  a.v = v;
+  a.w = w;
+  a.u = u;
+  a.y = y;
+  a.bf16 = dtype == WKV6_DTYPE_BF16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t ws_bytes = wkv6::wkv4_workspace_bytes(a);
+  void* ws = nullptr;
+  if (ws_bytes) {
+    const hipError_t e = hipMallocAsync(&ws, ws_bytes, s);
+    if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("workspace allocation: ") + hipGetErrorString(e));
+  }
+  const hipError_t e = wkv6::enqueue_wkv4(a, ws, s);
+  if (ws) {
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e == hipSuccess && ef != hipSuccess)
+      return fail(WKV6_ERR_HIP, std::string("workspace release: ") + hipGetErrorString(ef));
+  }
+  if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return WKV6_OK;
 }
 
 int wkv6_bwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k, const void* v,

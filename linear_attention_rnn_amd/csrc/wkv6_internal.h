@@ -23,6 +23,7 @@ struct FwdArgs {
   float* s_out;        // causal only: final state, same layout, or null
   bool bidirectional;
   bool bf16;
+  bool w_static = false;   // w_raw is [C]: one decay for every token (RWKV-5)
 };
 
 // Bytes of device workspace a call needs (0 when none).
@@ -53,5 +54,20 @@ struct BwdArgs {
 // Workspace of a backward call (always > 0) and its kernels (wkv6_backward.hip).
 size_t bwd_workspace_bytes(const BwdArgs& a);
 hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
+
+// RWKV-4 (wkv4_kernels.hip): per-channel normalised WKV, causal.
+struct Wkv4Args {
+  int64_t B, T, C;
+  const void* k;     // [B, T, C] float32 or bfloat16
+  const void* v;
+  const float* w;    // [C] decay rate (each step multiplies by exp(-w))
+  const float* u;    // [C] bonus of the current token
+  float* y;          // [B, T, C] float32
+  bool bf16;
+};
+
+// Workspace of an RWKV-4 call (segment summaries and carries; 0 if none).
+size_t wkv4_workspace_bytes(const Wkv4Args& a);
+hipError_t enqueue_wkv4(const Wkv4Args& a, void* workspace, hipStream_t stream);
 
 }  // namespace wkv6

@@ -109,6 +109,7 @@ struct Params {
   int H;
   int G;      // segments per sequence
   int SEGC;   // chunks per segment (the last segment may be shorter)
+  int w_static;   // w_raw is [C], the same decay for every token (RWKV-5; decode kernel)
 };
 
 constexpr int kSummFloats = PL + HS;
@@ -771,7 +772,8 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
 
 // npass / pass: the item's number of sweeps and this sweep's place among
 // them (for progress_priority).
-template <bool BF16, bool REV, int MODE, bool CARRY, bool SLOW>
+// WS: w_raw is one row of C values used for every token (RWKV-5).
+template <bool BF16, bool REV, int MODE, bool CARRY, bool SLOW, bool WS = false>
 __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int seg, int npass = 1,
                                       int pass = 0) {
   constexpr int SP = BF16 ? 2 : 3;
@@ -866,18 +868,22 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
   // unconditional, tokens past the segment reading zero.
   constexpr int ISZ = BF16 ? 2 : 4;
   const Rsrc rr = slice_rsrc(p.r, base, ISZ, T, C), rk = slice_rsrc(p.k, base, ISZ, T, C);
-  const Rsrc rv = slice_rsrc(p.v, base, ISZ, T, C), rw = slice_rsrc(p.w, base, ISZ, T, C);
+  const Rsrc rv = slice_rsrc(p.v, base, ISZ, T, C);
+  // a static decay (RWKV-5) is one row per head: every token reads row 0
+  const Rsrc rw = WS ? slice_rsrc(p.w, (int64_t)h * HS, ISZ, 1, C) : slice_rsrc(p.w, base, ISZ, T, C);
   const Rsrc ry = slice_rsrc(p.y, base, 4, T, C);
   Raw<BF16> buf[4];
   const int in_row0 = tok0 * Ci * ISZ, in_step = dir_rows * LC * Ci * ISZ;
   const int y_row0 = tok0 * Ci * 4 + 16 * g, y_step = dir_rows * LC * Ci * 4;
   auto fetch = [&](int ch) {
     // tokens past the segment read zero
-    const int off = tau < (int)min<int64_t>(LC, n - (int64_t)ch * LC) ? in_row0 + ch * in_step : kOffNone;
+    const bool in_seg = tau < (int)min<int64_t>(LC, n - (int64_t)ch * LC);
+    const int row = in_row0 + ch * in_step;
+    const int off = in_seg ? row : kOffNone;
     if (OUT) buf[0] = gload<BF16>(rr, off, g);
     buf[1] = gload<BF16>(rk, off, g);
     buf[2] = gload<BF16>(rv, off, g);
-    buf[3] = gload<BF16>(rw, off, g);
+    buf[3] = gload<BF16>(rw, in_seg ? (WS ? 0 : row) : kOffNone, g);
   };
   fetch(0);
 
@@ -1153,32 +1159,32 @@ __device__ __forceinline__ bool marker_set(const float* m) {
 
 // Outputs of one item with the sweeps on the fast path (SLOW = false: false
 // as soon as a chunk needs the slow path) or the general sweeps.
-template <bool BF16, bool BIDIR, bool CARRY, bool SLOW>
+template <bool BF16, bool BIDIR, bool CARRY, bool SLOW, bool WS>
 __device__ __forceinline__ bool run_item(const Params& p, char* lds, int bh, int seg) {
   if (BIDIR) {
     // the forward sweep runs even after the reverse one gave up (its result is
     // then recomputed anyway): one straight path keeps the registers of the
     // two sweeps apart
-    const bool ok = sweep<BF16, true, kOut, CARRY, SLOW>(p, lds, bh, seg, 2, 0);
+    const bool ok = sweep<BF16, true, kOut, CARRY, SLOW, WS>(p, lds, bh, seg, 2, 0);
     __syncthreads();   // partial rows of y written; LDS free for reuse
-    return sweep<BF16, false, kOutAcc, CARRY, SLOW>(p, lds, bh, seg, 2, 1) && ok;
+    return sweep<BF16, false, kOutAcc, CARRY, SLOW, WS>(p, lds, bh, seg, 2, 1) && ok;
   }
-  return sweep<BF16, false, kOut, CARRY, SLOW>(p, lds, bh, seg);
+  return sweep<BF16, false, kOut, CARRY, SLOW, WS>(p, lds, bh, seg);
 }
 
-template <bool BF16, bool BIDIR, bool CARRY>
+template <bool BF16, bool BIDIR, bool CARRY, bool WS>
 __global__ __launch_bounds__(NT, occupancy<BF16>()) void wkv_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
   const int bh = CARRY ? blockIdx.x / p.G : blockIdx.x, seg = CARRY ? blockIdx.x % p.G : 0;
-  if (!run_item<BF16, BIDIR, CARRY, false>(p, lds, bh, seg)) set_marker(item_marker(p, bh, seg));
+  if (!run_item<BF16, BIDIR, CARRY, false, WS>(p, lds, bh, seg)) set_marker(item_marker(p, bh, seg));
 }
 
-template <bool BF16, bool BIDIR, bool CARRY>
+template <bool BF16, bool BIDIR, bool CARRY, bool WS>
 __global__ __launch_bounds__(NT, 2) void wkv_fixup_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
   const int bh = CARRY ? blockIdx.x / p.G : blockIdx.x, seg = CARRY ? blockIdx.x % p.G : 0;
   if (!marker_set(item_marker(p, bh, seg))) return;
-  run_item<BF16, BIDIR, CARRY, true>(p, lds, bh, seg);
+  run_item<BF16, BIDIR, CARRY, true, WS>(p, lds, bh, seg);
 }
 
 // Segment summaries: end state and total decay of each segment in each sweep
@@ -1193,26 +1199,26 @@ __device__ __forceinline__ bool summary_item(int& bh, int& seg, int& rev, const 
   return rev ? seg > 0 : seg < p.G - 1;
 }
 
-template <bool BF16, bool BIDIR>
+template <bool BF16, bool BIDIR, bool WS>
 __global__ __launch_bounds__(NT, occupancy<BF16>()) void summary_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
   int bh, seg, rev;
   if (!summary_item<BF16, BIDIR>(bh, seg, rev, p)) return;
-  const bool ok = rev ? sweep<BF16, true, kState, false, false>(p, lds, bh, seg)
-                      : sweep<BF16, false, kState, false, false>(p, lds, bh, seg);
+  const bool ok = rev ? sweep<BF16, true, kState, false, false, WS>(p, lds, bh, seg)
+                      : sweep<BF16, false, kState, false, false, WS>(p, lds, bh, seg);
   if (!ok) set_marker(summary_marker(p, bh, seg, rev));
 }
 
-template <bool BF16, bool BIDIR>
+template <bool BF16, bool BIDIR, bool WS>
 __global__ __launch_bounds__(NT, 2) void summary_fixup_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
   int bh, seg, rev;
   if (!summary_item<BF16, BIDIR>(bh, seg, rev, p)) return;
   if (!marker_set(summary_marker(p, bh, seg, rev))) return;
   if (rev)
-    sweep<BF16, true, kState, false, true>(p, lds, bh, seg);
+    sweep<BF16, true, kState, false, true, WS>(p, lds, bh, seg);
   else
-    sweep<BF16, false, kState, false, true>(p, lds, bh, seg);
+    sweep<BF16, false, kState, false, true, WS>(p, lds, bh, seg);
 }
 
 // State passing through an empty sequence: s_out = s_in (zero without s_in).
@@ -1272,7 +1278,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(Params p) {
     for (int i = 0; i < 4; ++i) {
       r[i] = load_elem<BF16>(p.r, row + c0 + i);
       k[i] = load_elem<BF16>(p.k, row + c0 + i);
-      w[i] = ex2(-kLog2e * ex2(load_elem<BF16>(p.w, row + c0 + i) * kLog2e));
+      w[i] = ex2(-kLog2e * ex2(load_elem<BF16>(p.w, (p.w_static ? (int64_t)h * HS : row) + c0 + i) * kLog2e));
       v[i] = load_elem<BF16>(p.v, row + n0 + i);
     }
     // partial y over the thread's four rows, summed over the row groups of
@@ -1341,7 +1347,7 @@ Plan plan(const FwdArgs& a) {
   return pl;
 }
 
-template <bool BF16, bool BIDIR>
+template <bool BF16, bool BIDIR, bool WS>
 hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   Params p;
   p.r = a.r;
@@ -1358,27 +1364,33 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   p.H = (int)a.H;
   p.G = pl.G;
   p.SEGC = pl.SEGC;
+  p.w_static = a.w_static ? 1 : 0;
   const unsigned bh = (unsigned)(a.B * a.H);
   const dim3 block(NT);
   hipError_t e;
   if (pl.G > 1) {
     const dim3 grid(bh * pl.G * (BIDIR ? 2 : 1));
-    hipLaunchKernelGGL((summary_kernel<BF16, BIDIR>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((summary_kernel<BF16, BIDIR, WS>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((summary_fixup_kernel<BF16, BIDIR>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((summary_fixup_kernel<BF16, BIDIR, WS>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 grid(bh * pl.G);
   if (pl.G > 1) {
-    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true, WS>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, true, WS>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false, WS>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, false, WS>), grid, block, 0, s, p);
   }
   return hipGetLastError();
+}
+
+template <bool BF16, bool WS>
+hipError_t launch_ws(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
+  return a.bidirectional ? launch_t<BF16, true, WS>(a, pl, ws, s) : launch_t<BF16, false, WS>(a, pl, ws, s);
 }
 
 }  // namespace
@@ -1412,6 +1424,7 @@ hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream) {
     p.T = a.T;
     p.C = a.C;
     p.H = (int)a.H;
+    p.w_static = a.w_static ? 1 : 0;
     const dim3 grid((unsigned)(a.B * a.H));
     if (a.bf16)
       hipLaunchKernelGGL(decode_kernel<true>, grid, dim3(NT), 0, stream, p);
@@ -1421,10 +1434,8 @@ hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream) {
   }
   const Plan pl = plan(a);
   if (a.bf16)
-    return a.bidirectional ? launch_t<true, true>(a, pl, workspace, stream)
-                           : launch_t<true, false>(a, pl, workspace, stream);
-  return a.bidirectional ? launch_t<false, true>(a, pl, workspace, stream)
-                         : launch_t<false, false>(a, pl, workspace, stream);
+    return a.w_static ? launch_ws<true, true>(a, pl, workspace, stream) : launch_ws<true, false>(a, pl, workspace, stream);
+  return a.w_static ? launch_ws<false, true>(a, pl, workspace, stream) : launch_ws<false, false>(a, pl, workspace, stream);
 }
 
 }  // namespace wkv6

@@ -23,6 +23,14 @@ Recipe (identical for every consumer):
     those channels to a fixed value for every (b, t);
   * cast to float32; for bf16 workloads round r, k, v, w_raw to bfloat16 by
     round-to-nearest-even.  u always stays float32.
+
+The two older operators draw the same way with their own shapes:
+  * RWKV-5 (``random_inputs_wkv5``): r, k, v as above, then w_raw ~
+    Uniform(lo, hi) of shape [C] (one decay per channel), then u;
+  * RWKV-4 (``random_inputs_wkv4``): k ~ Normal(0, kscale^2) and v ~
+    Normal(0, 1) of shape [B, T, C], then the decay rates w ~ Uniform(w_lo,
+    w_hi) and the bonuses u ~ Normal(0, 1), both [C] float32; bf16 rounds k
+    and v only.
 """
 from __future__ import annotations
 
@@ -39,6 +47,8 @@ __all__ = [
     "random_inputs",
     "round_to_bf16",
     "bf16_bits",
+    "random_inputs_wkv5",
+    "random_inputs_wkv4",
 ]
 
 
@@ -173,3 +183,32 @@ def make_inputs(w: Workload | str) -> dict:
     return random_inputs(w.B, w.T, w.C, w.H, seed=w.seed, dtype=w.dtype,
                          wraw_lo=w.wraw_lo, wraw_hi=w.wraw_hi,
                          stuck_frac=w.stuck_frac, stuck_value=w.stuck_value)
+
+
+def random_inputs_wkv5(B: int, T: int, C: int, *, seed: int, dtype: str = "f32",
+                       wraw_lo: float = -6.0, wraw_hi: float = -0.5, scale: float = 0.5) -> dict:
+    """RWKV-5 inputs: r, k, v [B, T, C], one w_raw per channel [C], u [C]."""
+    rng = np.random.default_rng(seed)
+    r, k, v = (rng.normal(0.0, scale, size=(B, T, C)).astype(np.float32) for _ in range(3))
+    w_raw = rng.uniform(wraw_lo, wraw_hi, size=(C,)).astype(np.float32)
+    u = rng.normal(0.0, scale, size=(C,)).astype(np.float32)
+    if dtype == "bf16":
+        r, k, v, w_raw = (round_to_bf16(a) for a in (r, k, v, w_raw))
+    elif dtype != "f32":
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    return {"r": r, "k": k, "v": v, "w_raw": w_raw, "u": u}
+
+
+def random_inputs_wkv4(B: int, T: int, C: int, *, seed: int, dtype: str = "f32", kscale: float = 1.0,
+                       w_lo: float = 0.0, w_hi: float = 2.0) -> dict:
+    """RWKV-4 inputs: k, v [B, T, C]; decay rates w and bonuses u [C] float32."""
+    rng = np.random.default_rng(seed)
+    k = (rng.normal(size=(B, T, C)) * kscale).astype(np.float32)
+    v = rng.normal(size=(B, T, C)).astype(np.float32)
+    w = rng.uniform(w_lo, w_hi, size=(C,)).astype(np.float32)
+    u = rng.normal(size=(C,)).astype(np.float32)
+    if dtype == "bf16":
+        k, v = round_to_bf16(k), round_to_bf16(v)
+    elif dtype != "f32":
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    return {"k": k, "v": v, "w": w, "u": u}

@@ -41,7 +41,7 @@ def header_functions() -> list[str]:
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(wkv6_\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(wkv\d_\w+)\s*\(", text, flags=re.M)
 
 
 def lib() -> ctypes.CDLL:
@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.wkv6_fwd.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
                                ctypes.c_int, ctypes.c_int, vp]
         L.wkv6_fwd.restype = ctypes.c_int
+        L.wkv5_fwd.argtypes = L.wkv6_fwd.argtypes
+        L.wkv5_fwd.restype = ctypes.c_int
+        L.wkv4_fwd.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, ctypes.c_int, vp]
+        L.wkv4_fwd.restype = ctypes.c_int
         L.wkv6_fwd_state.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                      ctypes.c_int, vp]
         L.wkv6_fwd_state.restype = ctypes.c_int
@@ -90,20 +94,35 @@ def fwd_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, 
     return lib().wkv6_fwd(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype, stream)
 
 
+def fwd5_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, u: int,
+             y: int, mode: int, dtype: int, stream: int = 0) -> int:
+    """Direct call of wkv5_fwd (w_raw: C values) with integer addresses."""
+    return lib().wkv5_fwd(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype, stream)
+
+
+def fwd4_raw(B: int, T: int, C: int, k: int, v: int, w: int, u: int, y: int, dtype: int,
+             stream: int = 0) -> int:
+    """Direct call of wkv4_fwd with integer addresses."""
+    return lib().wkv4_fwd(B, T, C, k, v, w, u, y, dtype, stream)
+
+
 def fwd_state_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, u: int,
                   y: int, s_in: int, s_out: int, dtype: int, stream: int = 0) -> int:
     """Direct call of wkv6_fwd_state with integer addresses (0 = NULL)."""
     return lib().wkv6_fwd_state(B, T, C, H, r, k, v, w_raw, u, y, s_in, s_out, dtype, stream)
 
 
-def _check_inputs(r, k, v, w_raw, u):
+def _check_inputs(r, k, v, w_raw, u, w_static=False):
     import torch
 
     if r.dim() != 3:
         raise ValueError("r must be [B, T, C]")
     B, T, C = r.shape
     for name, t in (("k", k), ("v", v), ("w_raw", w_raw)):
-        if t.shape != r.shape or t.dtype != r.dtype:
+        if name == "w_raw" and w_static:
+            if t.numel() != C or t.dtype != r.dtype:
+                raise ValueError("w_raw must hold C values of r's dtype")
+        elif t.shape != r.shape or t.dtype != r.dtype:
             raise ValueError(f"{name} must match r in shape and dtype")
     if r.dtype == torch.float32:
         dtype = DTYPE_F32
@@ -179,6 +198,59 @@ def fwd(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
         raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
     st = fwd_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
                  u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, _stream_handle(stream, r.device))
+    if st != OK:
+        raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
+    return out
+
+
+def fwd5(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
+    """y = WKV5(r, k, v, w_raw, u): fwd with one decay for every token.
+
+    w_raw: contiguous CUDA tensor of C values (dtype of r), laid out [H, 64];
+    every token decays by exp(-exp(w_raw)).  Everything else as fwd.
+    """
+    import torch
+
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    B, T, C, dtype = _check_inputs(r, k, v, w_raw, u, w_static=True)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
+    elif out.shape != (B, T, C) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
+    st = fwd5_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
+                  u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, _stream_handle(stream, r.device))
+    if st != OK:
+        raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
+    return out
+
+
+def fwd4(k, v, w, u, out=None, stream=None):
+    """RWKV-4 WKV of k, v ([B, T, C], float32 or bfloat16) with per-channel
+    float32 decay rates w and bonuses u ([C]); returns float32 [B, T, C]."""
+    import torch
+
+    if k.dim() != 3 or v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must be [B, T, C] tensors of one dtype")
+    B, T, C = k.shape
+    if k.dtype == torch.float32:
+        dtype = DTYPE_F32
+    elif k.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    else:
+        raise ValueError("k and v must be float32 or bfloat16")
+    for name, t in (("w", w), ("u", u)):
+        if t.dtype != torch.float32 or t.numel() != C:
+            raise ValueError(f"{name} must be float32 with C elements")
+    for name, t in (("k", k), ("v", v), ("w", w), ("u", u)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
+    elif out.shape != (B, T, C) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
+    st = fwd4_raw(B, T, C, k.data_ptr(), v.data_ptr(), w.data_ptr(), u.data_ptr(), out.data_ptr(), dtype,
+                  _stream_handle(stream, k.device))
     if st != OK:
         raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
     return out

@@ -18,7 +18,7 @@ A = 0x10000  # fake, 16-byte aligned addresses: never dereferenced by these call
 
 def test_exports_every_declared_function():
     names = wkv6.header_functions()
-    assert set(names) == {"wkv6_fwd", "wkv6_fwd_state", "wkv6_bwd", "wkv6_status_str",
+    assert set(names) == {"wkv6_fwd", "wkv5_fwd", "wkv4_fwd", "wkv6_fwd_state", "wkv6_bwd", "wkv6_status_str",
                           "wkv6_last_error", "wkv6_abi_version"}
     L = wkv6.lib()
     for n in names:
@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert wkv6.abi_version() == 3
+    assert wkv6.abi_version() == 4
     assert wkv6.status_str(0) == "ok"
     texts = {wkv6.status_str(s) for s in range(5)}
     assert len(texts) == 5
@@ -166,3 +166,76 @@ def test_bwd_overlapping_output(out, other):
 
 def test_bwd_empty_batch_is_a_noop():
     assert _call_bwd(B=0, ptrs=[0] * 11) == wkv6.OK
+
+
+# ---- wkv5_fwd: wkv6_fwd's checks; w_raw holds only C values
+def _call5(B=2, T=8, C=128, H=2, ptrs=None, mode=0, dtype=0):
+    p = ptrs or [A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000]
+    return wkv6.fwd5_raw(B, T, C, H, *p, mode, dtype, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), wkv6.ERR_INVALID_ARG),
+    (dict(mode=2), wkv6.ERR_INVALID_ARG),
+    (dict(C=96, H=2), wkv6.ERR_UNSUPPORTED),
+    (dict(T=2 ** 31), wkv6.ERR_UNSUPPORTED),
+])
+def test_wkv5_rejects_bad_sizes(kw, status):
+    assert _call5(**kw) == status
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_wkv5_null_and_misaligned(which):
+    p = [A + 0x100000 * i for i in range(6)]
+    p[which] = 0
+    assert _call5(ptrs=p) == wkv6.ERR_INVALID_ARG
+    p[which] = A + 0x100000 * which + 4
+    assert _call5(ptrs=p) == wkv6.ERR_MISALIGNED
+
+
+def test_wkv5_output_overlap_counts_c_values_of_w():
+    p = [A + 0x100000 * i for i in range(6)]
+    p[5] = p[3] + 128 * 4 - 16          # y starts inside the 128 fp32 values of w_raw
+    assert _call5(ptrs=p) == wkv6.ERR_INVALID_ARG
+    assert "overlaps w_raw" in wkv6.last_error()
+
+
+def test_wkv5_empty_problem_is_a_noop():
+    assert _call5(B=0, ptrs=[0] * 6) == wkv6.OK
+    assert _call5(T=0, ptrs=[0] * 6) == wkv6.OK
+
+
+# ---- wkv4_fwd: per-channel operator, no heads
+def _call4(B=2, T=8, C=100, ptrs=None, dtype=0):
+    p = ptrs or [A + 0x100000 * i for i in range(5)]
+    return wkv6.fwd4_raw(B, T, C, *p, dtype, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), wkv6.ERR_INVALID_ARG),
+    (dict(T=-1), wkv6.ERR_INVALID_ARG),
+    (dict(C=-5), wkv6.ERR_INVALID_ARG),
+    (dict(dtype=3), wkv6.ERR_INVALID_ARG),
+    (dict(C=256 * 65536), wkv6.ERR_UNSUPPORTED),      # more channel blocks than grid rows
+    (dict(B=2 ** 31), wkv6.ERR_UNSUPPORTED),
+])
+def test_wkv4_rejects_bad_sizes(kw, status):
+    assert _call4(**kw) == status
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_wkv4_null_misaligned_overlap(which):
+    p = [A + 0x100000 * i for i in range(5)]
+    p[which] = 0
+    assert _call4(ptrs=p) == wkv6.ERR_INVALID_ARG
+    p[which] = A + 0x100000 * which + 8
+    assert _call4(ptrs=p) == wkv6.ERR_MISALIGNED
+    if which < 4:
+        p = [A + 0x100000 * i for i in range(5)]
+        p[4] = p[which] + 16
+        assert _call4(ptrs=p) == wkv6.ERR_INVALID_ARG and "overlaps" in wkv6.last_error()
+
+
+def test_wkv4_empty_problem_is_a_noop():
+    for kw in (dict(B=0), dict(T=0), dict(C=0)):
+        assert _call4(ptrs=[0] * 5, **kw) == wkv6.OK
