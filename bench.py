@@ -16,6 +16,14 @@ Prints ONE JSON line (rank 0) with, besides the throughput:
                 committed rocprofv3 counter runs measured for the same sources
   mfma          executed matrix-core work per call and its rate vs the bf16 peak
   cpu_baseline  the float64 CPU oracle timed on the host on a bounded sample
+
+--op selects another entry point of the library on the same workload shapes
+(default wkv6_fwd, the headline):
+  wkv6_bwd   the backward (gradients of sum(y * dy)); token-serial float32
+             vector arithmetic, so its roofline is the fp32 vector peak over
+             the algorithmic flops (12 N^2 per token, head and direction)
+  wkv5_fwd   RWKV-5: the forward with one decay per channel for every token
+  wkv4_fwd   RWKV-4: the normalised per-channel operator (always causal)
 """
 from __future__ import annotations
 
@@ -37,6 +45,8 @@ from linear_attention_rnn_amd import inputs as I  # noqa: E402
 HEADLINE = "image-base-bidir-bf16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak, published
+OPS = ("wkv6_fwd", "wkv6_bwd", "wkv5_fwd", "wkv4_fwd")
 MALL_BYTES = 256 << 20
 MFMA_FLOPS = 2 * 16 * 16 * 32  # one v_mfma_f32_16x16x32_bf16
 METRIC = "WKV6 fwd tokens/s (B·T/s) + % HBM roofline & MFMA util at N=64, 1 GPU"
@@ -130,26 +140,38 @@ def traffic_record(workload: str):
     return rec.get("bytes_per_call")
 
 
-def cpu_baseline(w: I.Workload, x: dict, budget_s: float = 20.0) -> dict:
-    """Time the float64 oracle on whole batch items of the same workload until
-    about `budget_s` seconds of CPU work, single-threaded."""
+def cpu_baseline(w: I.Workload, x: dict, budget_s: float = 20.0, op: str = "wkv6_fwd") -> dict:
+    """Time the float64 oracle of the op on whole batch items of the same
+    workload until about `budget_s` seconds of CPU work, single-threaded."""
     from threadpoolctl import threadpool_limits
 
-    from oracle import wkv6_ref
+    import oracle
+
+    def run(nb):
+        if op == "wkv6_fwd":
+            oracle.wkv6_ref(x["r"][:nb], x["k"][:nb], x["v"][:nb], x["w_raw"][:nb], x["u"], w.H, w.mode)
+        elif op == "wkv6_bwd":
+            oracle.wkv6_ref_backward(x["r"][:nb], x["k"][:nb], x["v"][:nb], x["w_raw"][:nb], x["u"],
+                                     x["dy"][:nb], w.H, w.mode)
+        elif op == "wkv5_fwd":
+            oracle.wkv5_ref(x["r"][:nb], x["k"][:nb], x["v"][:nb], x["w_raw"], x["u"], w.H, w.mode)
+        else:
+            oracle.wkv4_ref(x["k"][:nb], x["v"][:nb], x["w"], x["u"])
 
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        wkv6_ref(x["r"][:1], x["k"][:1], x["v"][:1], x["w_raw"][:1], x["u"], w.H, w.mode)
+        run(1)
         t1 = time.perf_counter() - t0
         nb = max(1, min(w.B, int(budget_s / max(t1, 1e-3))))
         if nb > 1:
             t0 = time.perf_counter()
-            wkv6_ref(x["r"][:nb], x["k"][:nb], x["v"][:nb], x["w_raw"][:nb], x["u"], w.H, w.mode)
+            run(nb)
             el = time.perf_counter() - t0
         else:
             el = t1
+    mode = "causal" if op == "wkv4_fwd" else w.mode
     return {"value": nb * w.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{nb} of {w.B} batch items (T={w.T}, C={w.C}, H={w.H}, {w.mode}, "
+            "sample": f"{nb} of {w.B} batch items (T={w.T}, C={w.C}, H={w.H}, {mode}, {op} oracle, "
                       f"float64 numpy recurrence, BLAS limited to 1 thread), {el:.1f} s"}
 
 
@@ -183,6 +205,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE, choices=[x.name for x in I.WORKLOADS])
+    ap.add_argument("--op", default="wkv6_fwd", choices=OPS,
+                    help="library entry point to time (default: the headline forward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-rotate", action="store_true",
@@ -203,32 +227,57 @@ def main() -> int:
 
     from linear_attention_rnn_amd import wkv6
 
-    def device_inputs(xs, dtype):
-        out = []
-        for key in ("r", "k", "v", "w_raw"):
-            a = xs[key]
-            if dtype == "bf16":
-                out.append(torch.from_numpy(I.bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda())
-            else:
-                out.append(torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda())
-        out.append(torch.from_numpy(np.ascontiguousarray(xs["u"], np.float32)).cuda())
-        return out
+    def dev(a, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(I.bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
 
     w = I.workload(args.workload)
-    x = I.make_inputs(w)
-    per_copy = w.algorithmic_bytes()
+    op = args.op
+    isz = 2 if w.dtype == "bf16" else 4
+    E = w.elements
+    mode = "causal" if op == "wkv4_fwd" else w.mode
+    if op == "wkv6_fwd":
+        x = I.make_inputs(w)
+        per_copy = w.algorithmic_bytes()
+    elif op == "wkv6_bwd":
+        x = I.make_inputs(w)
+        x["dy"] = np.random.default_rng(w.seed + 1000).normal(0.0, 0.5, size=(w.B, w.T, w.C)).astype(np.float32)
+        # read r, k, v, w_raw, dy and u; write dr, dk, dv, dw_raw and du
+        per_copy = E * (4 * isz + 4 + 16) + 2 * w.C * 4
+    elif op == "wkv5_fwd":
+        x = I.random_inputs_wkv5(w.B, w.T, w.C, seed=w.seed, dtype=w.dtype, wraw_lo=w.wraw_lo, wraw_hi=w.wraw_hi)
+        per_copy = E * (3 * isz + 4) + w.C * (isz + 4)
+    else:
+        x = I.random_inputs_wkv4(w.B, w.T, w.C, seed=w.seed, dtype=w.dtype)
+        per_copy = E * (2 * isz + 4) + 2 * w.C * 4
     ncopy = 1 if args.no_rotate else max(2, math.ceil(2 * MALL_BYTES / per_copy) + 1)
     sets = []
     for _ in range(ncopy):
-        d = device_inputs(x, w.dtype)
-        y = torch.empty((w.B, w.T, w.C), dtype=torch.float32, device="cuda")
+        if op == "wkv4_fwd":
+            d = [dev(x["k"], w.dtype), dev(x["v"], w.dtype), f32(x["w"]), f32(x["u"])]
+        else:
+            d = [dev(x[key], w.dtype) for key in ("r", "k", "v", "w_raw")] + [f32(x["u"])]
+        if op == "wkv6_bwd":
+            d.append(f32(x["dy"]))
+        y = torch.empty((w.B, w.T, w.C), dtype=torch.float32, device="cuda") if op != "wkv6_bwd" else None
         sets.append((d, y))
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
     def step(i):
         d, y = sets[i % ncopy]
-        wkv6.fwd(*d, w.H, w.mode, out=y, stream=stream)
+        if op == "wkv6_fwd":
+            wkv6.fwd(*d, w.H, w.mode, out=y, stream=stream)
+        elif op == "wkv6_bwd":
+            wkv6.bwd(*d, w.H, w.mode, stream=stream)
+        elif op == "wkv5_fwd":
+            wkv6.fwd5(*d, w.H, w.mode, out=y, stream=stream)
+        else:
+            wkv6.fwd4(*d, out=y, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -249,12 +298,34 @@ def main() -> int:
 
     alg_bytes = per_copy
     achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
-    n_mfma = mfma_count(w)
+    forward6 = op in ("wkv6_fwd", "wkv5_fwd")   # the chunked MFMA kernels
+    n_mfma = mfma_count(w) if forward6 else 0
     mfma_tflops = n_mfma * MFMA_FLOPS / (mean_ms * 1e-3) / 1e12
-    traffic = traffic_record(w.name)
+    traffic = traffic_record(w.name) if op == "wkv6_fwd" else None
+    if op == "wkv6_bwd":
+        # algorithmic fp32 vector work: per token, head and direction the state
+        # and adjoint updates (3 N^2 each: a product and a fused multiply-add
+        # per entry) and the dr, dk, dv contractions (2 N^2 each)
+        flops = 12 * w.N * w.N * w.B * w.T * w.H * (2 if w.mode == "bidirectional" else 1)
+        tflops = flops / (mean_ms * 1e-3) / 1e12
+        roofline = {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                    "kernel": "wkv6_bwd call: token-serial backward sweeps + u reduction",
+                    "mean_call_ms": mean_ms, "algorithmic_flops": flops,
+                    "hbm_achieved_GBps": achieved, "algorithmic_bytes": alg_bytes}
+    else:
+        kern = {"wkv6_fwd": "wkv6_fwd call: fast-path sweep kernel + fix-up kernel",
+                "wkv5_fwd": "wkv5_fwd call: fast-path sweep kernel + fix-up kernel",
+                "wkv4_fwd": "wkv4_fwd call: per-channel recurrence kernels"}[op]
+        if forward6 and plan_segments(w)[0] > 1:
+            kern += " + segment summary kernels"
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kern,
+                    "mean_call_ms": mean_ms, "algorithmic_bytes": alg_bytes}
+    metric = METRIC if op == "wkv6_fwd" else METRIC.replace("WKV6 fwd", op.upper().replace("_", " "))
 
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": w.tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -264,21 +335,18 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": "bf16" if (w.dtype == "bf16" and forward6) else "f32",
         "data": "synthetic (seeded numpy draws, recipe in linear_attention_rnn_amd/inputs.py)",
-        "config": {"workload": w.name, "mode": w.mode, "B": w.B, "T": w.T, "C": w.C, "H": w.H,
+        "config": {"workload": w.name, "op": op, "mode": mode, "B": w.B, "T": w.T, "C": w.C, "H": w.H,
                    "N": w.N, "inputs": w.dtype, "state_and_output": "f32",
                    "rotating_copies": ncopy, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "wkv6_fwd call: fast-path sweep kernel + fix-up kernel"
-                               + (" + segment summary kernels" if plan_segments(w)[0] > 1 else ""),
-                     "mean_call_ms": mean_ms, "algorithmic_bytes": alg_bytes},
-        "mfma": {"instructions": n_mfma, "executed_tflops": mfma_tflops,
-                 "util": mfma_tflops / MFMA_BF16_PEAK_TFLOPS, "peak_tflops": MFMA_BF16_PEAK_TFLOPS},
+        "roofline": roofline,
     }
+    if forward6:
+        out["mfma"] = {"instructions": n_mfma, "executed_tflops": mfma_tflops,
+                       "util": mfma_tflops / MFMA_BF16_PEAK_TFLOPS, "peak_tflops": MFMA_BF16_PEAK_TFLOPS}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget, op)
     print(json.dumps(out), flush=True)
     return 0
 
