@@ -16,7 +16,9 @@ Contents (all arithmetic in float64 on the exact input values):
 * ``wkv5_ref``         -- RWKV-5: the same operator with one decay per channel
                           for every token;
 * ``wkv4_ref``         -- RWKV-4: the normalised per-channel (vector-state)
-                          operator, in its recurrent form.
+                          operator, in its recurrent form;
+* ``group_norm_heads``, ``wkv6_gn_ref`` -- the per-head group normalisation
+                          and gate that follow the operator in a block.
 
 Every function here is pinned by tests that do not rely on the oracle itself
 (closed forms, a hand-worked example, invariants, brute force on tiny inputs);
@@ -24,6 +26,7 @@ there is no "parity unpinned" function in this package.
 """
 from .wkv6_oracle import decay, wkv6_ref, wkv6_bruteforce, wkv6_ref_backward, split_heads, merge_heads
 from .variants_oracle import wkv4_ref, wkv5_ref
+from .epilogue_oracle import group_norm_heads, wkv6_gn_ref
 
 __all__ = ["decay", "wkv6_ref", "wkv6_bruteforce", "wkv6_ref_backward", "split_heads", "merge_heads",
-           "wkv4_ref", "wkv5_ref"]
+           "wkv4_ref", "wkv5_ref", "group_norm_heads", "wkv6_gn_ref"]
