@@ -103,6 +103,40 @@ int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H,
              const float* u, float* y, int mode, int dtype, void* stream);
 
 /*
+ * wkv6_fwd_gn -- wkv6_fwd followed by the block's output normalisation and
+ * gate, fused into the kernel that produces the final outputs, with a bf16
+ * result: y is never written to memory.
+ *
+ *   out[b,t,c] = ( (y[b,t,c] - mean_h) / sqrt(var_h + eps) * gamma[c] + beta[c] ) * g[b,t,c]
+ *
+ * with mean_h and var_h (biased, divided by 64) over the 64 channels of the
+ * head h that holds c, for each (b, t): a per-head group normalisation
+ * ("RWKV Architecture" on llms.blog, section "RWKV-5 Eagle": group
+ * normalisation across the individual heads, and output gating by SiLU)
+ * and the gate g the spatial-mix block forms as SiLU of a linear map of its
+ * input (deepglint/rwkv-clip "What is the WKV mechanism" page, sections
+ * "Spatial-Mix Block Generating the WKV Inputs" and "Invocation Inside a
+ * Transformer-Style Block": the WKV output is normalised, then multiplied by
+ * g).  g is taken as that page computes it, i.e. after the SiLU.
+ *
+ *   r, k, v, w_raw, u, B, T, C, H, mode, dtype   as wkv6_fwd
+ *   g       device pointer to [B, T, C] values of `dtype`
+ *   gamma, beta   device pointers to C float32 values each ([H, 64])
+ *   eps     added to the variance; finite and >= 0 (else INVALID_ARG)
+ *   out     device pointer to a [B, T, C] bfloat16 output (16-bit words,
+ *           rounded to nearest even); must not overlap any input
+ *
+ * Workspace: a bidirectional call keeps the reverse sweep's float32 rows,
+ * B*T*C*4 bytes, plus 4 bytes per (batch item, head, segment) for its
+ * fix-up markers, and the segment summaries as in wkv6_fwd; allocated and
+ * released in stream order.  Execution and errors as wkv6_fwd.
+ */
+int wkv6_fwd_gn(int64_t B, int64_t T, int64_t C, int64_t H,
+                const void* r, const void* k, const void* v, const void* w_raw,
+                const float* u, const void* g, const float* gamma, const float* beta,
+                float eps, void* out, int mode, int dtype, void* stream);
+
+/*
  * wkv5_fwd -- the RWKV-5 ("Eagle") operator: the same matrix-state recurrence
  * and output as wkv6_fwd, with a decay that is a fixed per-channel parameter
  * instead of a per-token input ("RWKV Architecture" on llms.blog, section

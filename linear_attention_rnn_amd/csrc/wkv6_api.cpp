@@ -185,6 +185,36 @@ int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, co
   return run(a, static_cast<hipStream_t>(stream));
 }
 
+int wkv6_fwd_gn(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k, const void* v,
+                const void* w_raw, const float* u, const void* g, const float* gamma, const float* beta,
+                float eps, void* out, int mode, int dtype, void* stream) {
+  g_last_error.clear();
+  int st = check_sizes(B, T, C, H, mode, dtype);
+  if (st != WKV6_OK || B == 0 || T == 0) return st;
+  if (!(eps >= 0.f && eps <= 3.4e38f)) return fail(WKV6_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const void* ptrs[9] = {r, k, v, w_raw, u, g, gamma, beta, out};
+  const char* names[9] = {"r", "k", "v", "w_raw", "u", "g", "gamma", "beta", "out"};
+  for (int i = 0; i < 9; ++i)
+    if (!ptrs[i]) return fail(WKV6_ERR_INVALID_ARG, std::string("null pointer: ") + names[i]);
+  for (int i = 0; i < 9; ++i)
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16)
+      return fail(WKV6_ERR_MISALIGNED, std::string("pointer not 16-byte aligned: ") + names[i]);
+  const size_t elems = (size_t)B * (size_t)T * (size_t)C, isz = dtype == WKV6_DTYPE_BF16 ? 2 : 4;
+  const size_t nb[8] = {elems * isz, elems * isz, elems * isz, elems * isz, (size_t)C * 4,
+                        elems * isz, (size_t)C * 4, (size_t)C * 4};
+  for (int i = 0; i < 8; ++i)
+    if (overlaps(out, elems * 2, ptrs[i], nb[i]))
+      return fail(WKV6_ERR_INVALID_ARG, std::string("out overlaps ") + names[i]);
+  wkv6::FwdArgs a = make_args(B, T, C, H, r, k, v, w_raw, u, nullptr, mode, dtype);
+  a.epi = true;
+  a.out = static_cast<uint16_t*>(out);
+  a.gate = g;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.eps = eps;
+  return run(a, static_cast<hipStream_t>(stream));
+}
+
 int wkv4_fwd(int64_t B, int64_t T, int64_t C, const void* k, const void* v, const float* w, const float* u,
              float* y, int dtype, void* stream) {
   g_last_error.clear();

@@ -24,6 +24,14 @@ struct FwdArgs {
   bool bidirectional;
   bool bf16;
   bool w_static = false;   // w_raw is [C]: one decay for every token (RWKV-5)
+  // fused epilogue: out = (GroupNorm_head(y) * gamma + beta) * gate as bf16
+  // [B, T, C]; y is then not written (it may be null)
+  bool epi = false;
+  uint16_t* out = nullptr;
+  const void* gate = nullptr;   // [B, T, C], dtype of r
+  const float* gamma = nullptr;
+  const float* beta = nullptr;
+  float eps = 0.f;
 };
 
 // Bytes of device workspace a call needs (0 when none).

@@ -110,6 +110,13 @@ struct Params {
   int G;      // segments per sequence
   int SEGC;   // chunks per segment (the last segment may be shorter)
   int w_static;   // w_raw is [C], the same decay for every token (RWKV-5; decode kernel)
+  // fused epilogue (wkv6_fwd_gn): out = (GroupNorm(y) gamma + beta) gate, bf16
+  uint16_t* out;
+  const void* gate;     // [B, T, C], dtype of r
+  const float* gamma;   // [C]
+  const float* beta;    // [C]
+  float eps;
+  float* mark;          // one fix-up marker per (item, segment): y is not an output there
 };
 
 constexpr int kSummFloats = PL + HS;
@@ -126,6 +133,8 @@ struct SweepLds {
   static constexpr int kU = kBT + 4 * 64 * 4;
   static constexpr int kFlag = kU + 64 * 4;
   static constexpr int kBytes = kFlag + 16;
+  static constexpr int kGB = kBytes;                // fused epilogue: gamma[64], beta[64] of the head
+  static constexpr int kBytesEpi = kGB + 128 * 4;
 };
 
 
@@ -374,6 +383,87 @@ __device__ __forceinline__ void bstoref4(Rsrc r, int off, float a, float b, floa
   __builtin_amdgcn_raw_buffer_store_b128(q, r, off, 0, 0);
 }
 
+// Sum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48):
+// each swap hands a value to the partner row, so the two halves of its
+// result add to the pair's sum in every lane.
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Gate values of the lane's output channels 16 nt + 4 g .. + 3, nt = 0..3,
+// as loaded (bf16: 8 bytes per nt; fp32: 16 bytes).
+template <bool BF16>
+struct GateRaw {
+  uint32_t q[4][BF16 ? 2 : 4];
+};
+
+template <bool BF16>
+__device__ __forceinline__ GateRaw<BF16> load_gate(Rsrc rs, int off) {
+  GateRaw<BF16> g;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    if constexpr (BF16) {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, off + 32 * nt, 0, 0);
+      g.q[nt][0] = q[0];
+      g.q[nt][1] = q[1];
+    } else {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * nt, 0, 0);
+      g.q[nt][0] = q[0];
+      g.q[nt][1] = q[1];
+      g.q[nt][2] = q[2];
+      g.q[nt][3] = q[3];
+    }
+  }
+  return g;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float gate_at(const GateRaw<BF16>& g, int nt, int j) {
+  if constexpr (BF16)
+    return __uint_as_float((j & 1) ? (g.q[nt][j >> 1] & 0xFFFF0000u) : (g.q[nt][j >> 1] << 16));
+  else
+    return __uint_as_float(g.q[nt][j]);
+}
+
+// Fused epilogue of one token row held by the four lanes of a 16-lane column
+// (lane li + 16 g holds channels 16 nt + 4 g + j): per-head GroupNorm of y
+// (mean and variance over the 64 channels, eps inside the square root), the
+// per-channel affine gamma, beta, times the gate, rounded to bf16 (nearest
+// even) and stored.  Lanes of a token past the segment store nothing
+// (their byte offset lies outside the slice).
+template <bool BF16>
+__device__ __forceinline__ void gn_gate_store(const f32x4 (&Y)[4], const GateRaw<BF16>& gt, const float* sGm,
+                                              const float* sBt, int g, float eps, Rsrc ro, int ooff) {
+  float s = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) s += (Y[nt][0] + Y[nt][1]) + (Y[nt][2] + Y[nt][3]);
+  const float mean = rows_sum(s) * (1.f / 64.f);
+  float d[4][4], q = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      d[nt][j] = Y[nt][j] - mean;
+      q = fmaf(d[nt][j], d[nt][j], q);
+    }
+  const float rstd = __builtin_amdgcn_rsqf(fmaf(rows_sum(q), 1.f / 64.f, eps));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const float4 ga = *reinterpret_cast<const float4*>(sGm + 16 * nt + 4 * g);
+    const float4 be = *reinterpret_cast<const float4*>(sBt + 16 * nt + 4 * g);
+    const float o0 = fmaf(d[nt][0] * rstd, ga.x, be.x) * gate_at<BF16>(gt, nt, 0);
+    const float o1 = fmaf(d[nt][1] * rstd, ga.y, be.y) * gate_at<BF16>(gt, nt, 1);
+    const float o2 = fmaf(d[nt][2] * rstd, ga.z, be.z) * gate_at<BF16>(gt, nt, 2);
+    const float o3 = fmaf(d[nt][3] * rstd, ga.w, be.w) * gate_at<BF16>(gt, nt, 3);
+    const u32x2 w = {__builtin_bit_cast(uint32_t, round_pair(o0, o1)), __builtin_bit_cast(uint32_t, round_pair(o2, o3))};
+    __builtin_amdgcn_raw_buffer_store_b64(w, ro, ooff + 32 * nt, 0, 0);
+  }
+}
+
 // The lane's row: row_off is the row's byte offset in the slice.
 template <bool BF16>
 __device__ __forceinline__ Raw<BF16> gload(Rsrc rs, int row_off, int g) {
@@ -613,9 +703,12 @@ __device__ __forceinline__ void write_vT(__bf16* sV, const int (&c)[8], const Ra
 // keys of block J carry k 2^(E_J - Lin) (E_I: prefix at the end of block I);
 // the queries r 2^(Lex - E_I) of each key block and r 2^Lex of the state
 // product are built in phase C from the raw r and w words.
-template <bool BF16, int MODE, bool DIAG>
+// FIN: the final outputs go through the fused epilogue (gate rows at goff of
+// rg, bf16 rows at ooff of ro) instead of y.
+template <bool BF16, int MODE, bool DIAG, bool FIN = false>
 __device__ __forceinline__ void slow_chunk(const Params& p, char* lds, Raw<BF16> rraw, Raw<BF16> kraw,
-                                                     Raw<BF16> wraw, Rsrc ry, int yoff, int Lv, bool left) {
+                                                     Raw<BF16> wraw, Rsrc ry, int yoff, int Lv, bool left,
+                                                     Rsrc rg = Rsrc(), int goff = 0, Rsrc ro = Rsrc(), int ooff = 0) {
   constexpr int SP = BF16 ? 2 : 3;
   constexpr int SV = BF16 ? 1 : 3;
   constexpr bool OUT = MODE != kState;
@@ -738,7 +831,14 @@ __device__ __forceinline__ void slow_chunk(const Params& p, char* lds, Raw<BF16>
         o.z += yo.z;
         o.w += yo.w;
       }
-      bstoref4(ry, yoff + 64 * nt, o.x, o.y, o.z, o.w);
+      if constexpr (FIN)
+        Y[nt] = f32x4{o.x, o.y, o.z, o.w};
+      else
+        bstoref4(ry, yoff + 64 * nt, o.x, o.y, o.z, o.w);
+    }
+    if constexpr (FIN) {
+      const float* sGm = reinterpret_cast<const float*>(lds + L::kGB);
+      gn_gate_store<BF16>(Y, load_gate<BF16>(rg, goff), sGm, sGm + 64, g, p.eps, ro, ooff);
     }
   }
 }
@@ -773,7 +873,10 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
 // npass / pass: the item's number of sweeps and this sweep's place among
 // them (for progress_priority).
 // WS: w_raw is one row of C values used for every token (RWKV-5).
-template <bool BF16, bool REV, int MODE, bool CARRY, bool SLOW, bool WS = false>
+// EPI: the sweep that produces the final outputs (the causal sweep, or the
+// forward sweep of a bidirectional call) writes them through the fused
+// GroupNorm / gate epilogue as bf16 instead of writing y.
+template <bool BF16, bool REV, int MODE, bool CARRY, bool SLOW, bool WS = false, bool EPI = false>
 __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int seg, int npass = 1,
                                       int pass = 0) {
   constexpr int SP = BF16 ? 2 : 3;
@@ -809,6 +912,12 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
   const int Ci = (int)C;
 
   if (DIAG && tid < 64) sU[tid] = p.u[h * HS + tid];   // read after the first barrier
+  constexpr bool FIN = EPI && OUT && !REV;
+  float* sGm = reinterpret_cast<float*>(lds + L::kGB);
+  if (FIN && tid < 64) {
+    sGm[tid] = p.gamma[h * HS + tid];
+    sGm[64 + tid] = p.beta[h * HS + tid];
+  }
 
   // ---- state, rows 16J + 4g + j, columns 16 nt + li
   f32x4 S[4];
@@ -872,9 +981,14 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
   // a static decay (RWKV-5) is one row per head: every token reads row 0
   const Rsrc rw = WS ? slice_rsrc(p.w, (int64_t)h * HS, ISZ, 1, C) : slice_rsrc(p.w, base, ISZ, T, C);
   const Rsrc ry = slice_rsrc(p.y, base, 4, T, C);
+  // fused epilogue: gate rows (input dtype) and bf16 output rows, lane's channels 4g..
+  const Rsrc rg = FIN ? slice_rsrc(p.gate, base, ISZ, T, C) : Rsrc();
+  const Rsrc ro = FIN ? slice_rsrc(p.out, base, 2, T, C) : Rsrc();
   Raw<BF16> buf[4];
   const int in_row0 = tok0 * Ci * ISZ, in_step = dir_rows * LC * Ci * ISZ;
   const int y_row0 = tok0 * Ci * 4 + 16 * g, y_step = dir_rows * LC * Ci * 4;
+  const int g_row0 = in_row0 + 4 * g * ISZ;                                   // fused epilogue: gate rows
+  const int o_row0 = tok0 * Ci * 2 + 8 * g, o_step = dir_rows * LC * Ci * 2;   // and bf16 output rows
   auto fetch = [&](int ch) {
     // tokens past the segment read zero
     const bool in_seg = tau < (int)min<int64_t>(LC, n - (int64_t)ch * LC);
@@ -923,6 +1037,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // are dropped without a branch
     const int yoff = valid ? y_row0 + ch * y_step : kOffNone;
     f32x4 Y[4];
+    GateRaw<BF16> gt;
     if (OUT && active) {
       // the output accumulators start from the rows of y the reverse sweep
       // left (kOutAcc) or from zero; loaded here, a phase ahead of their use
@@ -964,6 +1079,8 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // ---- phase C (fast): scores of the key blocks up to the lane's own,
     // outputs
     if (OUT && active) {
+      // the gate rows for the fused epilogue, in flight during the products
+      if (FIN) gt = load_gate<BF16>(rg, valid ? g_row0 + ch * in_step : kOffNone);
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         const int I0 = 2 * pr;
@@ -997,8 +1114,12 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) Y[nt] = mma(rd8<SP>(sS, 1024 * nt + lo.a[ks]), q[ks], Y[nt]);
       }
+      if constexpr (FIN) {
+        gn_gate_store<BF16>(Y, gt, sGm, sGm + 64, g, p.eps, ro, valid ? o_row0 + ch * o_step : kOffNone);
+      } else {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bstoref4(ry, yoff + 64 * nt, Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
+        for (int nt = 0; nt < 4; ++nt) bstoref4(ry, yoff + 64 * nt, Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
+      }
     }
     if (ch == nch - 1) {
       if (OUT && !keep_state) {
@@ -1059,9 +1180,10 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
       }
       lds_barrier();
 
-      slow_chunk<BF16, MODE, DIAG>(p, lds, buf[0], buf[1], buf[3], ry,
-                                   valid ? y_row0 + ch * y_step : kOffNone, Lv,
-                                   left);
+      slow_chunk<BF16, MODE, DIAG, FIN>(p, lds, buf[0], buf[1], buf[3], ry,
+                                        valid ? y_row0 + ch * y_step : kOffNone, Lv, left, rg,
+                                        valid ? g_row0 + ch * in_step : kOffNone, ro,
+                                        valid ? o_row0 + ch * o_step : kOffNone);
       if (ch == nch - 1) {
         if (OUT && !keep_state) break;
       } else {
@@ -1139,7 +1261,9 @@ constexpr int occupancy() {
   return BF16 ? 3 : 2;
 }
 
+template <bool EPI = false>
 __device__ __forceinline__ float* item_marker(const Params& p, int bh, int seg) {
+  if constexpr (EPI) return p.mark + (int64_t)bh * p.G + seg;   // the fused epilogue writes no y
   const int b = bh / p.H, h = bh % p.H;
   return p.y + ((int64_t)b * p.T + (int64_t)seg * p.SEGC * LC) * p.C + (int64_t)h * HS;
 }
@@ -1159,32 +1283,33 @@ __device__ __forceinline__ bool marker_set(const float* m) {
 
 // Outputs of one item with the sweeps on the fast path (SLOW = false: false
 // as soon as a chunk needs the slow path) or the general sweeps.
-template <bool BF16, bool BIDIR, bool CARRY, bool SLOW, bool WS>
+template <bool BF16, bool BIDIR, bool CARRY, bool SLOW, bool WS, bool EPI>
 __device__ __forceinline__ bool run_item(const Params& p, char* lds, int bh, int seg) {
   if (BIDIR) {
     // the forward sweep runs even after the reverse one gave up (its result is
     // then recomputed anyway): one straight path keeps the registers of the
     // two sweeps apart
-    const bool ok = sweep<BF16, true, kOut, CARRY, SLOW, WS>(p, lds, bh, seg, 2, 0);
+    const bool ok = sweep<BF16, true, kOut, CARRY, SLOW, WS, EPI>(p, lds, bh, seg, 2, 0);
     __syncthreads();   // partial rows of y written; LDS free for reuse
-    return sweep<BF16, false, kOutAcc, CARRY, SLOW, WS>(p, lds, bh, seg, 2, 1) && ok;
+    return sweep<BF16, false, kOutAcc, CARRY, SLOW, WS, EPI>(p, lds, bh, seg, 2, 1) && ok;
   }
-  return sweep<BF16, false, kOut, CARRY, SLOW, WS>(p, lds, bh, seg);
+  return sweep<BF16, false, kOut, CARRY, SLOW, WS, EPI>(p, lds, bh, seg);
 }
 
-template <bool BF16, bool BIDIR, bool CARRY, bool WS>
+template <bool BF16, bool BIDIR, bool CARRY, bool WS, bool EPI>
 __global__ __launch_bounds__(NT, occupancy<BF16>()) void wkv_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
+  __shared__ __attribute__((aligned(16))) char lds[EPI ? SweepLds<BF16>::kBytesEpi : SweepLds<BF16>::kBytes];
   const int bh = CARRY ? blockIdx.x / p.G : blockIdx.x, seg = CARRY ? blockIdx.x % p.G : 0;
-  if (!run_item<BF16, BIDIR, CARRY, false, WS>(p, lds, bh, seg)) set_marker(item_marker(p, bh, seg));
+  if (EPI && threadIdx.x == 0) *item_marker<EPI>(p, bh, seg) = 0.f;   // clear a marker left by an earlier call
+  if (!run_item<BF16, BIDIR, CARRY, false, WS, EPI>(p, lds, bh, seg)) set_marker(item_marker<EPI>(p, bh, seg));
 }
 
-template <bool BF16, bool BIDIR, bool CARRY, bool WS>
+template <bool BF16, bool BIDIR, bool CARRY, bool WS, bool EPI>
 __global__ __launch_bounds__(NT, 2) void wkv_fixup_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
+  __shared__ __attribute__((aligned(16))) char lds[EPI ? SweepLds<BF16>::kBytesEpi : SweepLds<BF16>::kBytes];
   const int bh = CARRY ? blockIdx.x / p.G : blockIdx.x, seg = CARRY ? blockIdx.x % p.G : 0;
-  if (!marker_set(item_marker(p, bh, seg))) return;
-  run_item<BF16, BIDIR, CARRY, true, WS>(p, lds, bh, seg);
+  if (!marker_set(item_marker<EPI>(p, bh, seg))) return;
+  run_item<BF16, BIDIR, CARRY, true, WS, EPI>(p, lds, bh, seg);
 }
 
 // Segment summaries: end state and total decay of each segment in each sweep
@@ -1347,7 +1472,27 @@ Plan plan(const FwdArgs& a) {
   return pl;
 }
 
-template <bool BF16, bool BIDIR, bool WS>
+// Workspace: [segment summaries (G > 1)] [fused epilogue, bidirectional: the
+// reverse sweep's fp32 rows, B*T*C] [fused epilogue: one marker per item and
+// segment], each part 256-byte aligned.
+struct WsLayout {
+  size_t summ, ypart, mark, total;
+};
+
+WsLayout ws_layout(const FwdArgs& a, const Plan& pl) {
+  auto up = [](size_t n) { return (n + 255) & ~size_t(255); };
+  WsLayout l;
+  l.summ = 0;
+  size_t n = pl.G > 1 ? up((size_t)a.B * a.H * pl.G * 2 * kSummFloats * sizeof(float)) : 0;
+  l.ypart = n;
+  if (a.epi && a.bidirectional) n += up((size_t)a.B * a.T * a.C * sizeof(float));
+  l.mark = n;
+  if (a.epi) n += up((size_t)a.B * a.H * pl.G * sizeof(float));
+  l.total = n;
+  return l;
+}
+
+template <bool BF16, bool BIDIR, bool WS, bool EPI>
 hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   Params p;
   p.r = a.r;
@@ -1365,6 +1510,18 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   p.G = pl.G;
   p.SEGC = pl.SEGC;
   p.w_static = a.w_static ? 1 : 0;
+  p.out = a.out;
+  p.gate = a.gate;
+  p.gamma = a.gamma;
+  p.beta = a.beta;
+  p.eps = a.eps;
+  p.mark = nullptr;
+  if (EPI) {
+    const WsLayout l = ws_layout(a, pl);
+    char* wsb = static_cast<char*>(ws);
+    p.y = BIDIR ? reinterpret_cast<float*>(wsb + l.ypart) : nullptr;   // the reverse sweep's rows
+    p.mark = reinterpret_cast<float*>(wsb + l.mark);
+  }
   const unsigned bh = (unsigned)(a.B * a.H);
   const dim3 block(NT);
   hipError_t e;
@@ -1377,29 +1534,28 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   }
   const dim3 grid(bh * pl.G);
   if (pl.G > 1) {
-    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true, WS>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true, WS, EPI>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, true, WS>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, true, WS, EPI>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false, WS>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false, WS, EPI>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, false, WS>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, false, WS, EPI>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <bool BF16, bool WS>
+template <bool BF16, bool WS, bool EPI>
 hipError_t launch_ws(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
-  return a.bidirectional ? launch_t<BF16, true, WS>(a, pl, ws, s) : launch_t<BF16, false, WS>(a, pl, ws, s);
+  return a.bidirectional ? launch_t<BF16, true, WS, EPI>(a, pl, ws, s)
+                         : launch_t<BF16, false, WS, EPI>(a, pl, ws, s);
 }
 
 }  // namespace
 
 size_t workspace_bytes(const FwdArgs& a) {
-  if (a.T == 0 || (!a.bidirectional && a.T <= kDecodeMaxT)) return 0;
-  const Plan pl = plan(a);
-  if (pl.G == 1) return 0;
-  return (size_t)a.B * a.H * pl.G * 2 * kSummFloats * sizeof(float);
+  if (a.B == 0 || a.T == 0 || (!a.bidirectional && !a.epi && a.T <= kDecodeMaxT)) return 0;
+  return ws_layout(a, plan(a)).total;
 }
 
 hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream) {
@@ -1411,7 +1567,7 @@ hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream) {
     hipLaunchKernelGGL(state_copy_kernel, dim3(grid), dim3(NT), 0, stream, a.s_in, a.s_out, n);
     return hipGetLastError();
   }
-  if (!a.bidirectional && a.T <= kDecodeMaxT) {
+  if (!a.bidirectional && !a.epi && a.T <= kDecodeMaxT) {
     Params p{};
     p.r = a.r;
     p.k = a.k;
@@ -1433,9 +1589,15 @@ hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream) {
     return hipGetLastError();
   }
   const Plan pl = plan(a);
-  if (a.bf16)
-    return a.w_static ? launch_ws<true, true>(a, pl, workspace, stream) : launch_ws<true, false>(a, pl, workspace, stream);
-  return a.w_static ? launch_ws<false, true>(a, pl, workspace, stream) : launch_ws<false, false>(a, pl, workspace, stream);
+  // variants: plain, static decay (RWKV-5), fused epilogue (never both)
+  if (a.bf16) {
+    if (a.epi) return launch_ws<true, false, true>(a, pl, workspace, stream);
+    return a.w_static ? launch_ws<true, true, false>(a, pl, workspace, stream)
+                      : launch_ws<true, false, false>(a, pl, workspace, stream);
+  }
+  if (a.epi) return launch_ws<false, false, true>(a, pl, workspace, stream);
+  return a.w_static ? launch_ws<false, true, false>(a, pl, workspace, stream)
+                    : launch_ws<false, false, false>(a, pl, workspace, stream);
 }
 
 }  // namespace wkv6

@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
         L.wkv6_fwd.restype = ctypes.c_int
         L.wkv5_fwd.argtypes = L.wkv6_fwd.argtypes
         L.wkv5_fwd.restype = ctypes.c_int
+        L.wkv6_fwd_gn.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                  ctypes.c_int, ctypes.c_int, vp]
+        L.wkv6_fwd_gn.restype = ctypes.c_int
         L.wkv4_fwd.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, ctypes.c_int, vp]
         L.wkv4_fwd.restype = ctypes.c_int
         L.wkv6_fwd_state.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -98,6 +101,12 @@ def fwd5_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int,
              y: int, mode: int, dtype: int, stream: int = 0) -> int:
     """Direct call of wkv5_fwd (w_raw: C values) with integer addresses."""
     return lib().wkv5_fwd(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype, stream)
+
+
+def fwd_gn_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, u: int, g: int,
+               gamma: int, beta: int, eps: float, out: int, mode: int, dtype: int, stream: int = 0) -> int:
+    """Direct call of wkv6_fwd_gn with integer addresses."""
+    return lib().wkv6_fwd_gn(B, T, C, H, r, k, v, w_raw, u, g, gamma, beta, eps, out, mode, dtype, stream)
 
 
 def fwd4_raw(B: int, T: int, C: int, k: int, v: int, w: int, u: int, y: int, dtype: int,
@@ -220,6 +229,33 @@ def fwd5(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None)
         raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
     st = fwd5_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
                   u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, _stream_handle(stream, r.device))
+    if st != OK:
+        raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
+    return out
+
+
+def fwd_gn(r, k, v, w_raw, u, g, gamma, beta, H: int, mode: str = "causal", eps: float = 64e-5,
+           out=None, stream=None):
+    """bf16 [B, T, C] = (GroupNorm over each head's 64 channels of fwd(...))
+    * gamma + beta, times the gate g ([B, T, C], dtype of r); gamma, beta:
+    float32 [C].  y itself is never written."""
+    import torch
+
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    B, T, C, dtype = _check_inputs(r, k, v, w_raw, u)
+    if g.shape != r.shape or g.dtype != r.dtype or not g.is_cuda or not g.is_contiguous():
+        raise ValueError("g must be a contiguous GPU tensor like r")
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t.dtype != torch.float32 or t.numel() != C or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor of C values")
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.bfloat16, device=r.device)
+    elif out.shape != (B, T, C) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [B, T, C] tensor")
+    st = fwd_gn_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(), u.data_ptr(),
+                    g.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps), out.data_ptr(), _MODES[mode],
+                    dtype, _stream_handle(stream, r.device))
     if st != OK:
         raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
     return out

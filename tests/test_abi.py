@@ -18,7 +18,7 @@ A = 0x10000  # fake, 16-byte aligned addresses: never dereferenced by these call
 
 def test_exports_every_declared_function():
     names = wkv6.header_functions()
-    assert set(names) == {"wkv6_fwd", "wkv5_fwd", "wkv4_fwd", "wkv6_fwd_state", "wkv6_bwd", "wkv6_status_str",
+    assert set(names) == {"wkv6_fwd", "wkv6_fwd_gn", "wkv5_fwd", "wkv4_fwd", "wkv6_fwd_state", "wkv6_bwd", "wkv6_status_str",
                           "wkv6_last_error", "wkv6_abi_version"}
     L = wkv6.lib()
     for n in names:
@@ -239,3 +239,40 @@ def test_wkv4_null_misaligned_overlap(which):
 def test_wkv4_empty_problem_is_a_noop():
     for kw in (dict(B=0), dict(T=0), dict(C=0)):
         assert _call4(ptrs=[0] * 5, **kw) == wkv6.OK
+
+
+# ---- wkv6_fwd_gn: wkv6_fwd's checks plus the gate, affine and eps
+# pointers: r, k, v, w_raw, u, g, gamma, beta, out
+def _call_gn(B=2, T=8, C=128, H=2, ptrs=None, eps=1e-5, mode=0, dtype=0):
+    p = ptrs or [A + 0x100000 * i for i in range(9)]
+    return wkv6.fwd_gn_raw(B, T, C, H, *p[:8], eps, p[8], mode, dtype, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), wkv6.ERR_INVALID_ARG),
+    (dict(mode=4), wkv6.ERR_INVALID_ARG),
+    (dict(C=96, H=2), wkv6.ERR_UNSUPPORTED),
+    (dict(eps=-1.0), wkv6.ERR_INVALID_ARG),
+    (dict(eps=float("nan")), wkv6.ERR_INVALID_ARG),
+    (dict(eps=float("inf")), wkv6.ERR_INVALID_ARG),
+])
+def test_gn_rejects_bad_arguments(kw, status):
+    assert _call_gn(**kw) == status
+
+
+@pytest.mark.parametrize("which", range(9))
+def test_gn_null_misaligned_overlap(which):
+    p = [A + 0x100000 * i for i in range(9)]
+    p[which] = 0
+    assert _call_gn(ptrs=p) == wkv6.ERR_INVALID_ARG
+    p[which] = A + 0x100000 * which + 4
+    assert _call_gn(ptrs=p) == wkv6.ERR_MISALIGNED
+    if which != 8:
+        p = [A + 0x100000 * i for i in range(9)]
+        p[8] = p[which] + 16
+        assert _call_gn(ptrs=p) == wkv6.ERR_INVALID_ARG and "overlaps" in wkv6.last_error()
+
+
+def test_gn_empty_problem_is_a_noop():
+    assert _call_gn(B=0, ptrs=[0] * 9) == wkv6.OK
+    assert _call_gn(T=0, ptrs=[0] * 9) == wkv6.OK
