@@ -39,6 +39,7 @@
 // (shuffles, then LDS across the four waves).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "wkv6_internal.h"
 
@@ -61,10 +62,21 @@ struct BwdParams {
   float* dv;
   float* dw;
   float* dr_tmp;   // REV: the reversed problem's dr between the passes
-  float* du_part;  // [B][C] per batch item (u gradient, causal part only)
+  float* du_part;  // [B][G][C] per batch item and segment (u gradient, causal part only)
   int64_t T;
   int64_t C;
   int H;
+  // A sequence may be cut into G segments of SEGL sweep positions each (the
+  // last may be shorter), handled by different workgroups.  Carries of the
+  // launch's direction, [B*H][G][64][64] (entry [c][n]) and [B*H][G][64]:
+  int G;
+  int64_t SEGL;
+  float* Sl;    // the segment's state after its last token, from zero
+  float* Gl;    // the segment's adjoint before its first token, from zero after its last
+  float* Wl;    // sum over the segment of lambda = ln w, per channel
+  float* Sin;   // state entering the segment (from the earlier segments)
+  float* Gin;   // adjoint after the segment's last token (from the later segments)
+  float* sig;   // per channel: sum over the segment of r dr - k dk
 };
 
 // Four consecutive channels of one input row, widened to float32.
@@ -83,6 +95,14 @@ __device__ __forceinline__ typename Raw4<BF16>::type ld4(const void* p, int64_t 
     return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
   else
     return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float ld1(const void* p, int64_t i) {
+  if constexpr (BF16)
+    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
+  else
+    return static_cast<const float*>(p)[i];
 }
 
 __device__ __forceinline__ float4 widen(float4 x) { return x; }
@@ -177,11 +197,13 @@ struct Pre {
 };
 
 // REV: the later-token part of a bidirectional call (reversed token order,
-// no u term, outputs accumulated).
-template <bool BF16, bool REV>
+// no u term, outputs accumulated).  SUM: a segment's summaries only (its
+// state from zero, its adjoint from zero, its total log decay) for the carry
+// kernel.  One workgroup per (batch item, head, segment).
+template <bool BF16, bool REV, bool SUM>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   __shared__ Smem sm;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
   const int b = bh / p.H, h = bh % p.H;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // token steps: rows c0 .. c0 + 3 and columns n0 .. n0 + 3 of the state
@@ -189,7 +211,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   // staging and output: token ts of the block, channels cc .. cc + 3
   const int ts = t >> 4, cc = 4 * (t & 15);
   const int64_t T = p.T, C = p.C;
-  const int nblk = (int)((T + TB - 1) / TB);
+  // the segment's sweep positions [q0, q1); block bi covers q0 + bi TB ..
+  const int64_t q0 = (int64_t)seg * p.SEGL, q1 = T < q0 + p.SEGL ? T : q0 + p.SEGL;
+  const int nblk = (int)((q1 - q0 + TB - 1) / TB);
+  const bool segmented = p.G > 1;
   const int64_t head = (int64_t)b * T * C + (int64_t)h * HS;
   auto row_of = [&](int64_t q) {   // sweep position -> element offset of the token's head row
     return head + (REV ? T - 1 - q : q) * C;
@@ -213,17 +238,32 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   // Every prefetch reads a valid row: positions past the end repeat the last
   // token and staging zeroes them, so the loads need no branch (a branch
   // would make the compiler wait for them at once).
+  auto pos = [&](int bi) { return q0 + (int64_t)bi * TB + ts; };
   auto at_q = [&](int bi) {
-    const int64_t q = (int64_t)bi * TB + ts;
-    return row_of(q < T ? q : T - 1) + cc;
+    const int64_t q = pos(bi);
+    return row_of(q < q1 ? q : q1 - 1) + cc;
   };
+  // SUM: the segment's total log decay, per staged channel (summed over the
+  // staged tokens, then over the workgroup at the end)
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+  auto add_lam = [&](bool ok, float4 lam) {
+    if (ok) {
+      lsum[0] += lam.x;
+      lsum[1] += lam.y;
+      lsum[2] += lam.z;
+      lsum[3] += lam.w;
+    }
+  };
+  const bool run_fwd = !SUM || seg < p.G - 1;   // summaries: the state of every segment but the last,
+  const bool run_bwd = !SUM || seg > 0;         // the adjoint of every segment but the first
+  const bool lam_in_fwd = run_fwd;              // the pass that also sums the decay
   auto stage_dyv = [&](float4 dy, float4 v) {
     const float d = row_sum(fmaf(dy.x, v.x, fmaf(dy.y, v.y, fmaf(dy.z, v.z, dy.w * v.w))));
     if (cc == 0) sm.dyv[ts] = d;
   };
 
   // ---------------- pass 1: forward sweep, state S, dr
-  {
+  if (run_fwd) {
     Pre<BF16> x;
     float4 old_dr;   // REV: the causal part already in p.dr, for the block whose dr leaves next
     auto load = [&](int bi) {
@@ -231,11 +271,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       x.k = ld4<BF16>(p.k, o);
       x.w = ld4<BF16>(p.w, o);
       x.v = ld4<BF16>(p.v, o);
-      x.dy = f4(p.dy + o);
+      if (!SUM) x.dy = f4(p.dy + o);
     };
     auto out = [&](int bi) {   // dr of block bi: staged partial sums plus u k (dy . v)
-      const int64_t q = (int64_t)bi * TB + ts;
-      if (q >= T) return;
+      const int64_t q = pos(bi);
+      if (q >= q1) return;
       const float4 a = f4(&sm.oa[ts][cc]), k = f4(&sm.k[ts][cc]);
       const float d = sm.dyv[ts];
       const float4 dr = make_float4(fmaf(uc[0] * k.x, d, a.x), fmaf(uc[1] * k.y, d, a.y), fmaf(uc[2] * k.z, d, a.z),
@@ -249,23 +289,39 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) S[i][j] = 0.f;
+    if (!SUM && segmented) {   // the state the earlier segments hand over
+      const float* si = p.Sin + ((int64_t)bh * p.G + seg) * (HS * HS);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 q = f4(si + (c0 + i) * HS + n0);
+        S[i][0] = q.x;
+        S[i][1] = q.y;
+        S[i][2] = q.z;
+        S[i][3] = q.w;
+      }
+    }
     load(0);
     for (int bi = 0; bi < nblk; ++bi) {
       __syncthreads();   // the previous block's token steps are done with the staging arrays
-      if (bi > 0) out(bi - 1);
+      if (!SUM && bi > 0) out(bi - 1);
       {
-        const bool ok = (int64_t)bi * TB + ts < T;
-        const float4 k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v)), dy = keep(ok, x.dy);
+        const bool ok = pos(bi) < q1;
+        const float4 k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v));
         float4 lam, w;
         decay(widen(x.w), lam, w);
         st4(&sm.k[ts][cc], k);
         st4(&sm.w[ts][cc], w);
         st4(&sm.v[ts][cc], v);
-        st4(&sm.dy[ts][cc], dy);
-        stage_dyv(dy, v);
+        if (SUM) {
+          add_lam(ok, lam);
+        } else {
+          const float4 dy = keep(ok, x.dy);
+          st4(&sm.dy[ts][cc], dy);
+          stage_dyv(dy, v);
+        }
       }
       __syncthreads();
-      if (REV) old_dr = f4(p.dr + at_q(bi));
+      if (REV && !SUM) old_dr = f4(p.dr + at_q(bi));
       load(bi + 1 < nblk ? bi + 1 : bi);
       struct Tk {
         float4 k, w, v, dy;
@@ -275,7 +331,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         e.k = f4(&sm.k[tt][c0]);
         e.w = f4(&sm.w[tt][c0]);
         e.v = f4(&sm.v[tt][n0]);
-        e.dy = f4(&sm.dy[tt][n0]);
+        if (!SUM) e.dy = f4(&sm.dy[tt][n0]);
         return e;
       };
       Tk nx = rd(0);
@@ -283,11 +339,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       for (int tt = 0; tt < TB; ++tt) {
         const Tk e = nx;
         if (tt + 1 < TB) nx = rd(tt + 1);   // the next token's operands are in flight during this one
-        float a[4];
+        if (!SUM) {
+          float a[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a[i] = fmaf(S[i][0], e.dy.x, fmaf(S[i][1], e.dy.y, fmaf(S[i][2], e.dy.z, S[i][3] * e.dy.w)));
-        sm.oa[tt][c0 + ri] = row_sums4(a, hi, hq);
+          for (int i = 0; i < 4; ++i)
+            a[i] = fmaf(S[i][0], e.dy.x, fmaf(S[i][1], e.dy.y, fmaf(S[i][2], e.dy.z, S[i][3] * e.dy.w)));
+          sm.oa[tt][c0 + ri] = row_sums4(a, hi, hq);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ki = at(e.k, i), wi = at(e.w, i);
@@ -298,23 +356,31 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
       }
     }
-    __syncthreads();
-    out(nblk - 1);
+    if (SUM) {
+      float* so = p.Sl + ((int64_t)bh * p.G + seg) * (HS * HS);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st4(so + (c0 + i) * HS + n0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
+    } else {
+      __syncthreads();
+      out(nblk - 1);
+    }
   }
   __syncthreads();   // pass 1's dr rows are written before pass 2 reads them
 
   // ---------------- pass 2: backward sweep, adjoint G, dk, dv, dw_raw
-  {
+  if (run_bwd) {
     Pre<BF16> x;
     float4 old_k, old_v, old_w;   // REV: the causal parts already in the outputs, for the block that leaves next
     auto load = [&](int bi) {
       const int64_t o = at_q(bi);
       x.r = ld4<BF16>(p.r, o);
-      x.k = ld4<BF16>(p.k, o);
       x.w = ld4<BF16>(p.w, o);
-      x.v = ld4<BF16>(p.v, o);
       x.dy = f4(p.dy + o);
-      x.dr = f4(drw + o);
+      if (!SUM) {
+        x.k = ld4<BF16>(p.k, o);
+        x.v = ld4<BF16>(p.v, o);
+        x.dr = f4(drw + o);
+      }
     };
     auto load_old = [&](int bi) {
       const int64_t o = at_q(bi);
@@ -324,12 +390,12 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     };
     float du[4] = {0.f, 0.f, 0.f, 0.f};
     auto out = [&](int bi) {   // dk, dv, dw_raw of block bi
-      const int64_t q = (int64_t)bi * TB + ts;
+      const int64_t q = pos(bi);
       const float4 r = f4(&sm.r[ts][cc]), k = f4(&sm.k[ts][cc]), dy = f4(&sm.dy[ts][cc]);
       const float d = sm.dyv[ts];
       const float4 ru = make_float4(r.x * uc[0], r.y * uc[1], r.z * uc[2], r.w * uc[3]);
       const float ruk = row_sum(fmaf(ru.x, k.x, fmaf(ru.y, k.y, fmaf(ru.z, k.z, ru.w * k.w))));
-      if (q >= T) return;
+      if (q >= q1) return;
       const float4 lam = f4(&sm.lam[ts][cc]), D = f4(&sm.ob[ts][cc]);
       float4 dk = f4(&sm.oa[ts][cc]);
       float4 dv = add4(add4(f4(&sm.ov[ts][0][cc]), f4(&sm.ov[ts][1][cc])),
@@ -357,30 +423,45 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) G[i][j] = 0.f;
+    if (!SUM && segmented) {   // the adjoint the later segments hand back
+      const float* gi = p.Gin + ((int64_t)bh * p.G + seg) * (HS * HS);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 q = f4(gi + (c0 + i) * HS + n0);
+        G[i][0] = q.x;
+        G[i][1] = q.y;
+        G[i][2] = q.z;
+        G[i][3] = q.w;
+      }
+    }
     // D (running dlambda without the u term), its compensation, and r dr of
     // the token after the current one
     float D = 0.f, Dc = 0.f, rdr_next = 0.f;   // for row c0 + ri
     load(nblk - 1);
     for (int bi = nblk - 1; bi >= 0; --bi) {
       __syncthreads();   // the previous block's token steps are done with the staging arrays
-      if (bi < nblk - 1) out(bi + 1);
+      if (!SUM && bi < nblk - 1) out(bi + 1);
       {
-        const bool ok = (int64_t)bi * TB + ts < T;
-        const float4 r = keep(ok, widen(x.r)), k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v));
-        const float4 dy = keep(ok, x.dy), dr = keep(ok, x.dr);
+        const bool ok = pos(bi) < q1;
+        const float4 r = keep(ok, widen(x.r)), dy = keep(ok, x.dy);
         float4 lam, w;
         decay(widen(x.w), lam, w);
         st4(&sm.r[ts][cc], r);
-        st4(&sm.k[ts][cc], k);
         st4(&sm.w[ts][cc], w);
-        st4(&sm.lam[ts][cc], lam);
-        st4(&sm.x[ts][cc], make_float4(r.x * dr.x, r.y * dr.y, r.z * dr.z, r.w * dr.w));
-        st4(&sm.v[ts][cc], v);
         st4(&sm.dy[ts][cc], dy);
-        stage_dyv(dy, v);
+        if (SUM) {
+          if (!lam_in_fwd) add_lam(ok, lam);
+        } else {
+          const float4 k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v)), dr = keep(ok, x.dr);
+          st4(&sm.k[ts][cc], k);
+          st4(&sm.lam[ts][cc], lam);
+          st4(&sm.x[ts][cc], make_float4(r.x * dr.x, r.y * dr.y, r.z * dr.z, r.w * dr.w));
+          st4(&sm.v[ts][cc], v);
+          stage_dyv(dy, v);
+        }
       }
       __syncthreads();
-      if (REV) load_old(bi);
+      if (REV && !SUM) load_old(bi);
       load(bi > 0 ? bi - 1 : 0);
       struct Tk {
         float4 r, k, w, v, dy;
@@ -389,14 +470,16 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       auto rd = [&](int tt) {
         Tk e;
         e.r = f4(&sm.r[tt][c0]);
-        e.k = f4(&sm.k[tt][c0]);
         e.w = f4(&sm.w[tt][c0]);
-        e.v = f4(&sm.v[tt][n0]);
         e.dy = f4(&sm.dy[tt][n0]);
-        e.d = sm.dyv[tt];
-        e.ki = sm.k[tt][c0 + ri];
-        e.rdri = sm.x[tt][c0 + ri];
-        e.rui = sm.r[tt][c0 + ri] * u_ri;
+        if (!SUM) {
+          e.k = f4(&sm.k[tt][c0]);
+          e.v = f4(&sm.v[tt][n0]);
+          e.d = sm.dyv[tt];
+          e.ki = sm.k[tt][c0 + ri];
+          e.rdri = sm.x[tt][c0 + ri];
+          e.rui = sm.r[tt][c0 + ri] * u_ri;
+        }
         return e;
       };
       Tk nx = rd(TB - 1);
@@ -404,24 +487,26 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       for (int tt = TB - 1; tt >= 0; --tt) {
         const Tk e = nx;
         if (tt > 0) nx = rd(tt - 1);   // the next token's operands are in flight during this one
-        float a[4];
+        if (!SUM) {
+          float a[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a[i] = fmaf(G[i][0], e.v.x, fmaf(G[i][1], e.v.y, fmaf(G[i][2], e.v.z, G[i][3] * e.v.w)));
-        const float dk = fmaf(e.rui, e.d, row_sums4(a, hi, hq));
-        // D += r_{q+1} dr_{q+1} - k_q dk_q, compensated
-        const float term = fmaf(-e.ki, dk, rdr_next) - Dc;
-        const float sum = D + term;
-        Dc = (sum - D) - term;
-        D = sum;
-        rdr_next = e.rdri;
-        sm.oa[tt][c0 + ri] = dk;
-        sm.ob[tt][c0 + ri] = D;
-        float b[4];
+          for (int i = 0; i < 4; ++i)
+            a[i] = fmaf(G[i][0], e.v.x, fmaf(G[i][1], e.v.y, fmaf(G[i][2], e.v.z, G[i][3] * e.v.w)));
+          const float dk = fmaf(e.rui, e.d, row_sums4(a, hi, hq));
+          // D += r_{q+1} dr_{q+1} - k_q dk_q, compensated
+          const float term = fmaf(-e.ki, dk, rdr_next) - Dc;
+          const float sum = D + term;
+          Dc = (sum - D) - term;
+          D = sum;
+          rdr_next = e.rdri;
+          sm.oa[tt][c0 + ri] = dk;
+          sm.ob[tt][c0 + ri] = D;
+          float b[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b[j] = fmaf(G[0][j], e.k.x, fmaf(G[1][j], e.k.y, fmaf(G[2][j], e.k.z, G[3][j] * e.k.w)));
-        sm.ov[tt][wave][n0 + cj] = rows_sums4(b);
+          for (int j = 0; j < 4; ++j)
+            b[j] = fmaf(G[0][j], e.k.x, fmaf(G[1][j], e.k.y, fmaf(G[2][j], e.k.z, G[3][j] * e.k.w)));
+          sm.ov[tt][wave][n0 + cj] = rows_sums4(b);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ri_ = at(e.r, i), wi = at(e.w, i);
@@ -432,24 +517,117 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
       }
     }
-    __syncthreads();
-    out(0);
-    if (!REV) {   // du over the threads that share the channels: rows of the wave, then the waves
+    if (SUM) {
+      float* go = p.Gl + ((int64_t)bh * p.G + seg) * (HS * HS);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) du[i] = rows_sum(du[i]);
+      for (int i = 0; i < 4; ++i) st4(go + (c0 + i) * HS + n0, make_float4(G[i][0], G[i][1], G[i][2], G[i][3]));
+    } else {
       __syncthreads();
-      if (lane < 16) st4(&sm.ov[0][wave][cc], make_float4(du[0], du[1], du[2], du[3]));
-      __syncthreads();
-      if (t < 16) {
-        const float4 s = add4(add4(f4(&sm.ov[0][0][cc]), f4(&sm.ov[0][1][cc])),
-                              add4(f4(&sm.ov[0][2][cc]), f4(&sm.ov[0][3][cc])));
-        st4(p.du_part + (int64_t)b * C + h * HS + cc, s);
+      out(0);
+      // the segment's sum of r dr - k dk: D at its first token plus that token's r dr
+      if (segmented && (lane & 3) == 0) p.sig[((int64_t)bh * p.G + seg) * HS + c0 + ri] = (D - Dc) + rdr_next;
+      if (!REV) {   // du over the threads that share the channels: rows of the wave, then the waves
+#pragma unroll
+        for (int i = 0; i < 4; ++i) du[i] = rows_sum(du[i]);
+        __syncthreads();
+        if (lane < 16) st4(&sm.ov[0][wave][cc], make_float4(du[0], du[1], du[2], du[3]));
+        __syncthreads();
+        if (t < 16) {
+          const float4 s = add4(add4(f4(&sm.ov[0][0][cc]), f4(&sm.ov[0][1][cc])),
+                                add4(f4(&sm.ov[0][2][cc]), f4(&sm.ov[0][3][cc])));
+          st4(p.du_part + ((int64_t)b * p.G + seg) * C + h * HS + cc, s);
+        }
       }
+    }
+  }
+  if (SUM) {   // the segment's total log decay per channel: over the staging rows, then the waves
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lsum[i] = rows_sum(lsum[i]);
+    __syncthreads();
+    if (lane < 16) st4(&sm.ov[0][wave][cc], make_float4(lsum[0], lsum[1], lsum[2], lsum[3]));
+    __syncthreads();
+    if (t < 16) {
+      const float4 s4 = add4(add4(f4(&sm.ov[0][0][cc]), f4(&sm.ov[0][1][cc])),
+                             add4(f4(&sm.ov[0][2][cc]), f4(&sm.ov[0][3][cc])));
+      st4(p.Wl + ((int64_t)bh * p.G + seg) * HS + cc, s4);
     }
   }
 }
 
-// du[c] = sum over batch items of the per-item parts.
+// Segment carries of one direction, per (batch item, head): the state
+// entering segment g, Sin[g] = e^{Wl[g-1]} Sin[g-1] + Sl[g-1] from zero, and
+// the adjoint after segment g's last token, Gin[g] = e^{Wl[g+1]} Gin[g+1] +
+// Gl[g+1] from zero after the last segment (the decays scale the rows: the
+// key channel).  Thread t: row t / 4, columns 16 (t % 4) .. + 15.
+__global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p) {
+  const int bh = blockIdx.x, t = threadIdx.x;
+  const int c = t >> 2, n0 = 16 * (t & 3);
+  const int64_t base = (int64_t)bh * p.G;
+  float acc[16];
+  auto step = [&](const float* src, int gs, float* dst) {   // dst = acc, then acc = e^{Wl[gs]} acc + src
+    float4* o = reinterpret_cast<float4*>(dst);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+    if (!src) return;
+    const float e = ex2(p.Wl[(base + gs) * HS + c] * kLog2e);
+    const float4* q = reinterpret_cast<const float4*>(src);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 x = q[j];
+      acc[4 * j] = fmaf(e, acc[4 * j], x.x);
+      acc[4 * j + 1] = fmaf(e, acc[4 * j + 1], x.y);
+      acc[4 * j + 2] = fmaf(e, acc[4 * j + 2], x.z);
+      acc[4 * j + 3] = fmaf(e, acc[4 * j + 3], x.w);
+    }
+  };
+  const int64_t off = (int64_t)c * HS + n0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int g = 0; g < p.G; ++g)
+    step(g + 1 < p.G ? p.Sl + (base + g) * (HS * HS) + off : nullptr, g, p.Sin + (base + g) * (HS * HS) + off);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int g = p.G - 1; g >= 0; --g)
+    step(g > 0 ? p.Gl + (base + g) * (HS * HS) + off : nullptr, g, p.Gin + (base + g) * (HS * HS) + off);
+}
+
+// The decay gradient's running sum reaches past a segment: for token j of
+// segment g, D_j also holds the sum over every later segment of r dr - k dk
+// (per direction, in that direction's sweep order).  dw_raw_j += lambda_j
+// times those sums.  One workgroup per (batch item, head, causal segment);
+// thread t: channel t % 64, tokens t / 64, + 4, ...
+template <bool BF16>
+__global__ __launch_bounds__(NT) void bwd_dwfix_kernel(BwdParams p, const float* sigc, const float* sigr) {
+  __shared__ float sT[64][HS];   // [0]: causal tail of this segment; [1 + g']: reverse tail of reverse segment g'
+  const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
+  const int b = bh / p.H, h = bh % p.H;
+  const int t = threadIdx.x;
+  const int64_t base = (int64_t)bh * p.G;
+  if (t < HS) {
+    float acc = 0.f;
+    for (int g2 = p.G - 1; g2 > seg; --g2) acc += sigc[(base + g2) * HS + t];
+    sT[0][t] = acc;
+    if (sigr) {
+      acc = 0.f;
+      for (int g2 = p.G - 1; g2 >= 0; --g2) {
+        sT[1 + g2][t] = acc;
+        acc += sigr[(base + g2) * HS + t];
+      }
+    }
+  }
+  __syncthreads();
+  const int c = t & (HS - 1);
+  const int64_t t_lo = (int64_t)seg * p.SEGL, t_hi = p.T < t_lo + p.SEGL ? p.T : t_lo + p.SEGL;
+  for (int64_t tok = t_lo + (t >> 6); tok < t_hi; tok += NT / HS) {
+    const int64_t o = ((int64_t)b * p.T + tok) * p.C + (int64_t)h * HS + c;
+    float tail = sT[0][c];
+    if (sigr) tail += sT[1 + (int)((p.T - 1 - tok) / p.SEGL)][c];
+    const float lam = -ex2(ld1<BF16>(p.w, o) * kLog2e);
+    p.dw[o] = fmaf(lam, tail, p.dw[o]);
+  }
+}
+
+// du[c] = sum over batch items and segments of the parts.
 __global__ __launch_bounds__(NT) void du_reduce_kernel(const float* __restrict__ part, float* __restrict__ du,
                                                        int64_t B, int64_t C) {
   const int64_t c = (int64_t)blockIdx.x * NT + threadIdx.x;
@@ -461,11 +639,96 @@ __global__ __launch_bounds__(NT) void du_reduce_kernel(const float* __restrict__
 
 }  // namespace
 
+namespace {
+
+constexpr int kMaxSeg = 63;   // the dw fix-up keeps one row per reverse segment in LDS
+
+struct BwdPlan {
+  int G;
+  int64_t SEGL;
+};
+
+// Fewer items (batch x head) than CUs: cut the sequences into segments of
+// whole 16-token blocks, at least 64 tokens each, for about three resident
+// workgroups per CU.  With every CU already holding an item, segments only
+// add the summary pass (about half a main pass), which costs more than the
+// extra occupancy gains (measured: B8 T4096 H32 is fastest unsegmented,
+// B4 T4096 H16 fastest with 12 segments).
+BwdPlan bwd_plan(const BwdArgs& a) {
+  const int64_t bh = a.B * a.H;
+  int64_t G = 1;
+  if (const char* e = getenv("WKV6_BWD_SEGMENTS")) {
+    G = atoi(e);
+  } else if (bh < 256) {
+    G = (768 + bh - 1) / bh;
+  }
+  const int64_t gmax = a.T / 64 > 1 ? a.T / 64 : 1;
+  if (G > gmax) G = gmax;
+  if (G > kMaxSeg) G = kMaxSeg;
+  if (G < 1) G = 1;
+  BwdPlan pl;
+  pl.SEGL = ((a.T + G - 1) / G + TB - 1) / TB * TB;
+  pl.G = (int)((a.T + pl.SEGL - 1) / pl.SEGL);
+  return pl;
+}
+
+struct BwdWs {
+  size_t du, drtmp, dir[2], total;   // byte offsets; dir: carries of each direction
+};
+
+size_t up256(size_t n) { return (n + 255) & ~size_t(255); }
+
+BwdWs bwd_ws(const BwdArgs& a, const BwdPlan& pl) {
+  BwdWs w;
+  size_t n = 0;
+  w.du = n;
+  n += up256((size_t)a.B * pl.G * a.C * 4);
+  w.drtmp = n;
+  if (a.bidirectional) n += up256((size_t)a.B * a.T * a.C * 4);
+  const size_t per = pl.G > 1 ? (size_t)a.B * a.H * pl.G * (4 * HS * HS + 2 * HS) * 4 : 0;
+  for (int d = 0; d < 2; ++d) {
+    w.dir[d] = n;
+    if (d == 0 || a.bidirectional) n += up256(per);
+  }
+  w.total = n;
+  return w;
+}
+
+void set_carries(BwdParams& p, char* ws, size_t off, int64_t bh, int G) {
+  float* f = reinterpret_cast<float*>(ws + off);
+  const size_t st = (size_t)bh * G * HS * HS, vec = (size_t)bh * G * HS;
+  p.Sl = f;
+  p.Gl = f + st;
+  p.Sin = f + 2 * st;
+  p.Gin = f + 3 * st;
+  p.Wl = f + 4 * st;
+  p.sig = f + 4 * st + vec;
+}
+
+template <bool BF16, bool REV, bool SUM>
+void launch_one(dim3 grid, hipStream_t s, const BwdParams& p) {
+  hipLaunchKernelGGL((bwd_kernel<BF16, REV, SUM>), grid, dim3(NT), 0, s, p);
+}
+
+void launch_bwd(bool bf16, bool rev, bool sum, dim3 grid, hipStream_t s, const BwdParams& p) {
+  if (bf16) {
+    if (rev)
+      sum ? launch_one<true, true, true>(grid, s, p) : launch_one<true, true, false>(grid, s, p);
+    else
+      sum ? launch_one<true, false, true>(grid, s, p) : launch_one<true, false, false>(grid, s, p);
+  } else {
+    if (rev)
+      sum ? launch_one<false, true, true>(grid, s, p) : launch_one<false, true, false>(grid, s, p);
+    else
+      sum ? launch_one<false, false, true>(grid, s, p) : launch_one<false, false, false>(grid, s, p);
+  }
+}
+
+}  // namespace
+
 size_t bwd_workspace_bytes(const BwdArgs& a) {
   if (a.T == 0) return 0;
-  size_t n = (size_t)a.B * a.C * 4;                                 // du parts
-  if (a.bidirectional) n += (size_t)a.B * a.T * a.C * 4 + 256;      // reversed problem's dr
-  return n;
+  return bwd_ws(a, bwd_plan(a)).total;
 }
 
 hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t s) {
@@ -475,7 +738,10 @@ hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t s) {
                        (int64_t)0, (int64_t)a.C);
     return hipGetLastError();
   }
-  BwdParams p;
+  const BwdPlan pl = bwd_plan(a);
+  const BwdWs lay = bwd_ws(a, pl);
+  char* ws = static_cast<char*>(workspace);
+  BwdParams p{};
   p.r = a.r;
   p.k = a.k;
   p.v = a.v;
@@ -486,29 +752,39 @@ hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t s) {
   p.dk = a.dk;
   p.dv = a.dv;
   p.dw = a.dw_raw;
-  p.du_part = static_cast<float*>(workspace);
-  p.dr_tmp = a.bidirectional
-                 ? reinterpret_cast<float*>((reinterpret_cast<uintptr_t>(p.du_part + a.B * a.C) + 255) & ~uintptr_t(255))
-                 : nullptr;
+  p.du_part = reinterpret_cast<float*>(ws + lay.du);
+  p.dr_tmp = a.bidirectional ? reinterpret_cast<float*>(ws + lay.drtmp) : nullptr;
   p.T = a.T;
   p.C = a.C;
   p.H = (int)a.H;
-  const dim3 grid((unsigned)(a.B * a.H));
-  if (a.bf16)
-    hipLaunchKernelGGL((bwd_kernel<true, false>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_kernel<false, false>), grid, block, 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.bidirectional) {
+  p.G = pl.G;
+  p.SEGL = pl.SEGL;
+  const int64_t bh = a.B * a.H;
+  const dim3 grid((unsigned)(bh * pl.G));
+  hipError_t e;
+  float* sig[2] = {nullptr, nullptr};
+  for (int d = 0; d < (a.bidirectional ? 2 : 1); ++d) {
+    const bool rev = d == 1;
+    if (pl.G > 1) {
+      set_carries(p, ws, lay.dir[d], bh, pl.G);
+      sig[d] = p.sig;
+      launch_bwd(a.bf16, rev, true, grid, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)bh), block, 0, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    launch_bwd(a.bf16, rev, false, grid, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (pl.G > 1) {
     if (a.bf16)
-      hipLaunchKernelGGL((bwd_kernel<true, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL(bwd_dwfix_kernel<true>, grid, block, 0, s, p, sig[0], sig[1]);
     else
-      hipLaunchKernelGGL((bwd_kernel<false, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL(bwd_dwfix_kernel<false>, grid, block, 0, s, p, sig[0], sig[1]);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(du_reduce_kernel, dim3((unsigned)((a.C + NT - 1) / NT)), block, 0, s, p.du_part, a.du,
-                     (int64_t)a.B, (int64_t)a.C);
+                     (int64_t)(a.B * pl.G), (int64_t)a.C);
   return hipGetLastError();
 }
 
