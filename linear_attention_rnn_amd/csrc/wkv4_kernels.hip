@@ -15,6 +15,9 @@
 //   output:  q = max(p, u + k),     y = (e^{p-q} a + e^{u+k-q} v) / (e^{p-q} b + e^{u+k-q})
 //   update:  p' = max(p - w, k),    a <- e^{p-w-p'} a + e^{k-p'} v,  b likewise,  p <- p'
 //
+// In each pair of factors the larger exponent's is exactly 1, so a step
+// takes two exponentials (and one reciprocal) instead of four.
+//
 // The recurrence is linear in (a, b): a segment of L tokens run from zero
 // yields a summary (A, Bs, P), and a state entering the segment leaves it
 // decayed by e^{-wL} and plus that summary.  Long sequences over few
@@ -26,6 +29,7 @@
 // segment, y = block of 256 channels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "wkv6_internal.h"
 
@@ -63,23 +67,32 @@ struct St {
   float a, b, p;
 };
 
+// Scale factors of two exponents x and z against their maximum: the larger
+// one's factor is exactly 1, so one exponential serves both.
+__device__ __forceinline__ void pair_scale(float x, float z, float& fx, float& fz) {
+  const float d = x - z;
+  const float e = e2(-fabsf(d));
+  const bool xbig = d >= 0.f;   // also when x = z; a NaN d falls to the other side
+  fx = xbig ? 1.f : e;
+  fz = xbig ? e : 1.f;
+}
+
 // One token: output (OUT) then update; exponents in log2 units (x log2 e).
 template <bool OUT>
 __device__ __forceinline__ float step(St& s, float k, float v, float wl, float ul) {
   float y = 0.f;
   const float kl = k * kL2e;
   if (OUT) {
-    const float uk = ul + kl;
-    const float q = fmaxf(s.p, uk);
-    const float e1 = e2(s.p - q), e2v = e2(uk - q);
+    float e1, e2v;   // 2^(p - q), 2^(u + k - q) with q = max(p, u + k)
+    pair_scale(s.p, ul + kl, e1, e2v);
     y = fmaf(e1, s.a, e2v * v) * __builtin_amdgcn_rcpf(fmaf(e1, s.b, e2v));
   }
   const float pw = s.p - wl;
-  const float p2 = fmaxf(pw, kl);
-  const float f1 = e2(pw - p2), f2 = e2(kl - p2);
+  float f1, f2;      // 2^(p - w - p'), 2^(k - p') with p' = max(p - w, k)
+  pair_scale(pw, kl, f1, f2);
   s.a = fmaf(f1, s.a, f2 * v);
   s.b = fmaf(f1, s.b, f2);
-  s.p = p2;
+  s.p = fmaxf(pw, kl);
   return y;
 }
 
@@ -183,6 +196,7 @@ Plan4 plan4(const Wkv4Args& a) {
   // least 64 tokens
   const int64_t lanes = a.B * a.C;
   int64_t G = (262144 + lanes - 1) / lanes;
+  if (const char* e = getenv("WKV4_SEGMENTS")) G = atoi(e);
   const int64_t gmax = a.T / 64 > 1 ? a.T / 64 : 1;
   if (G > gmax) G = gmax;
   if (G < 1) G = 1;
