@@ -83,7 +83,9 @@ extern "C" {
  * sequence into segments handled by different workgroups (more when the
  * sequences are long enough); such calls take a temporary device workspace
  * of B*H*segments*2*(64*64+64)*4 bytes for the segment summaries, allocated
- * and released in stream order (hipMallocAsync / hipFreeAsync on `stream`).
+ * and released in stream order on `stream`, from a memory pool the library
+ * creates on each device (hipMemPoolCreate) and that keeps freed blocks for
+ * later calls until the process ends.
  * Other calls allocate nothing.  y is written in place while the call runs:
  * a bidirectional call first stores the later-token part of every row and
  * then adds the rest, so y must not be read before the stream has run the
@@ -179,7 +181,7 @@ int wkv5_fwd(int64_t B, int64_t T, int64_t C, int64_t H,
  * largest exponent seen so far, so any finite keys work in float32.  Long
  * sequences over few channels are cut into segments; such calls take a
  * temporary device workspace of 2 * B * segments * 3 * C * 4 bytes,
- * allocated and released in stream order (hipMallocAsync / hipFreeAsync).
+ * allocated and released in stream order from the library's pool (as wkv6_fwd).
  * Ownership, execution and errors as wkv6_fwd (status codes, nothing
  * enqueued on a failed check, values not checked); B, T or C = 0 is a no-op.
  */
@@ -242,9 +244,15 @@ int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H,
  *           batch and the tokens.  T == 0 sets it to zero.
  *
  * B == 0 is a no-op.  The outputs must not overlap one another or any input
- * (INVALID_ARG).  The call takes a stream-ordered workspace (B*C*4 bytes,
- * plus B*T*C*4 in bidirectional mode) and runs two token-by-token passes per
- * (batch, head) in float32; errors otherwise as for wkv6_fwd.
+ * (INVALID_ARG).  The call runs two token-by-token passes per (batch, head)
+ * in float32.  With fewer than 256 (batch, head) pairs it cuts each sequence
+ * into up to 63 segments (whole 16-token blocks, at least 64 tokens each):
+ * a summary pass then gives each segment its entering state and leaving
+ * adjoint, and a last pass completes the decay gradient across segments.
+ * Workspace (stream-ordered, from the library's pool as for wkv6_fwd):
+ * B*segments*C*4 bytes, plus B*T*C*4 in bidirectional mode, plus
+ * B*H*segments*(4*64*64 + 2*64)*4 per direction when segmented.  Errors
+ * otherwise as for wkv6_fwd.
  */
 int wkv6_bwd(int64_t B, int64_t T, int64_t C, int64_t H,
              const void* r, const void* k, const void* v, const void* w_raw,

@@ -563,32 +563,51 @@ __global__ __launch_bounds__(NT) void bwd_carry_kernel(BwdParams p) {
   const int bh = blockIdx.x, t = threadIdx.x;
   const int c = t >> 2, n0 = 16 * (t & 3);
   const int64_t base = (int64_t)bh * p.G;
-  float acc[16];
-  auto step = [&](const float* src, int gs, float* dst) {   // dst = acc, then acc = e^{Wl[gs]} acc + src
-    float4* o = reinterpret_cast<float4*>(dst);
+  const int64_t off = (int64_t)c * HS + n0;
+  constexpr int64_t PLS = HS * HS;
+  // One direction: for each segment in order, store the running value, then
+  // fold the segment in (acc = e^{Wl} acc + summary).  The next segment's
+  // summary and decay are loaded before the current store, so the loads of
+  // consecutive segments overlap.
+  auto run = [&](const float* summ, float* dst, int g0, int dg) {
+    float acc[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
-    if (!src) return;
-    const float e = ex2(p.Wl[(base + gs) * HS + c] * kLog2e);
-    const float4* q = reinterpret_cast<const float4*>(src);
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+    float4 cur[4];
+    float e = 0.f;
+    auto fetch = [&](int g, float4 (&x)[4], float& ex) {
+      const float4* q = reinterpret_cast<const float4*>(summ + (base + g) * PLS + off);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 x = q[j];
-      acc[4 * j] = fmaf(e, acc[4 * j], x.x);
-      acc[4 * j + 1] = fmaf(e, acc[4 * j + 1], x.y);
-      acc[4 * j + 2] = fmaf(e, acc[4 * j + 2], x.z);
-      acc[4 * j + 3] = fmaf(e, acc[4 * j + 3], x.w);
+      for (int j = 0; j < 4; ++j) x[j] = q[j];
+      ex = ex2(p.Wl[(base + g) * HS + c] * kLog2e);
+    };
+    fetch(g0, cur, e);
+    for (int i = 0, g = g0; i < p.G; ++i, g += dg) {
+      float4 nxt[4];
+      float en = 0.f;
+      const bool more = i + 2 < p.G;   // the last segment's summary is never folded in
+      if (more) fetch(g + dg, nxt, en);
+      float4* o = reinterpret_cast<float4*>(dst + (base + g) * PLS + off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+      if (i + 1 < p.G) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[4 * j] = fmaf(e, acc[4 * j], cur[j].x);
+          acc[4 * j + 1] = fmaf(e, acc[4 * j + 1], cur[j].y);
+          acc[4 * j + 2] = fmaf(e, acc[4 * j + 2], cur[j].z);
+          acc[4 * j + 3] = fmaf(e, acc[4 * j + 3], cur[j].w);
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+        e = en;
+      }
     }
   };
-  const int64_t off = (int64_t)c * HS + n0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-  for (int g = 0; g < p.G; ++g)
-    step(g + 1 < p.G ? p.Sl + (base + g) * (HS * HS) + off : nullptr, g, p.Sin + (base + g) * (HS * HS) + off);
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-  for (int g = p.G - 1; g >= 0; --g)
-    step(g > 0 ? p.Gl + (base + g) * (HS * HS) + off : nullptr, g, p.Gin + (base + g) * (HS * HS) + off);
+  run(p.Sl, p.Sin, 0, 1);            // state entering each segment, first to last
+  run(p.Gl, p.Gin, p.G - 1, -1);     // adjoint after each segment, last to first
 }
 
 // The decay gradient's running sum reaches past a segment: for token j of
@@ -618,23 +637,53 @@ __global__ __launch_bounds__(NT) void bwd_dwfix_kernel(BwdParams p, const float*
   __syncthreads();
   const int c = t & (HS - 1);
   const int64_t t_lo = (int64_t)seg * p.SEGL, t_hi = p.T < t_lo + p.SEGL ? p.T : t_lo + p.SEGL;
-  for (int64_t tok = t_lo + (t >> 6); tok < t_hi; tok += NT / HS) {
-    const int64_t o = ((int64_t)b * p.T + tok) * p.C + (int64_t)h * HS + c;
-    float tail = sT[0][c];
-    if (sigr) tail += sT[1 + (int)((p.T - 1 - tok) / p.SEGL)][c];
-    const float lam = -ex2(ld1<BF16>(p.w, o) * kLog2e);
-    p.dw[o] = fmaf(lam, tail, p.dw[o]);
+  constexpr int U = 8;   // tokens per thread in flight
+  for (int64_t t0 = t_lo + (t >> 6); t0 < t_hi; t0 += U * (NT / HS)) {
+    float wr[U], dw[U];
+    int64_t o[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      int64_t tok = t0 + j * (NT / HS);
+      tok = tok < t_hi ? tok : t_hi - 1;   // past the end: reread the last row (not stored)
+      o[j] = ((int64_t)b * p.T + tok) * p.C + (int64_t)h * HS + c;
+      wr[j] = ld1<BF16>(p.w, o[j]);
+      dw[j] = p.dw[o[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t tok = t0 + j * (NT / HS);
+      if (tok < t_hi) {
+        float tail = sT[0][c];
+        if (sigr) tail += sT[1 + (int)((p.T - 1 - tok) / p.SEGL)][c];
+        p.dw[o[j]] = fmaf(-ex2(wr[j] * kLog2e), tail, dw[j]);
+      }
+    }
   }
 }
 
-// du[c] = sum over batch items and segments of the parts.
+// du[c] = sum over the rows (batch items x segments) of the parts: 64
+// channels per workgroup, four threads per channel each taking every fourth
+// row with eight loads in flight, then the four partial sums through LDS.
 __global__ __launch_bounds__(NT) void du_reduce_kernel(const float* __restrict__ part, float* __restrict__ du,
-                                                       int64_t B, int64_t C) {
-  const int64_t c = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (c >= C) return;
-  float s = 0.f;
-  for (int64_t b = 0; b < B; ++b) s += part[b * C + c];
-  du[c] = s;
+                                                       int64_t R, int64_t C) {
+  __shared__ float sp[NT / HS][HS];
+  const int cl = threadIdx.x & (HS - 1), q = threadIdx.x / HS;
+  const int64_t c = (int64_t)blockIdx.x * HS + cl;
+  float acc = 0.f;
+  if (c < C) {
+    int64_t r = q;
+    for (; r + 28 < R; r += 32) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = part[(r + 4 * j) * C + c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += x[j];
+    }
+    for (; r < R; r += 4) acc += part[r * C + c];
+  }
+  sp[q][cl] = acc;
+  __syncthreads();
+  if (q == 0 && c < C) du[c] = (sp[0][cl] + sp[1][cl]) + (sp[2][cl] + sp[3][cl]);
 }
 
 }  // namespace
@@ -734,7 +783,7 @@ size_t bwd_workspace_bytes(const BwdArgs& a) {
 hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t s) {
   const dim3 block(NT);
   if (a.T == 0) {   // no tokens: du = 0 (a sum over nothing)
-    hipLaunchKernelGGL(du_reduce_kernel, dim3((unsigned)((a.C + NT - 1) / NT)), block, 0, s, nullptr, a.du,
+    hipLaunchKernelGGL(du_reduce_kernel, dim3((unsigned)((a.C + HS - 1) / HS)), block, 0, s, nullptr, a.du,
                        (int64_t)0, (int64_t)a.C);
     return hipGetLastError();
   }
@@ -783,7 +832,7 @@ hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t s) {
       hipLaunchKernelGGL(bwd_dwfix_kernel<false>, grid, block, 0, s, p, sig[0], sig[1]);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(du_reduce_kernel, dim3((unsigned)((a.C + NT - 1) / NT)), block, 0, s, p.du_part, a.du,
+  hipLaunchKernelGGL(du_reduce_kernel, dim3((unsigned)((a.C + HS - 1) / HS)), block, 0, s, p.du_part, a.du,
                      (int64_t)(a.B * pl.G), (int64_t)a.C);
   return hipGetLastError();
 }
