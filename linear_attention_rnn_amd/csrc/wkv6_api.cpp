@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <mutex>
@@ -223,7 +224,7 @@ int wkv6_fwd_gn(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const
   g_last_error.clear();
   int st = check_sizes(B, T, C, H, mode, dtype);
   if (st != WKV6_OK || B == 0 || T == 0) return st;
-  if (!(eps >= 0.f && eps <= 3.4e38f)) return fail(WKV6_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!(std::isfinite(eps) && eps >= 0.f)) return fail(WKV6_ERR_INVALID_ARG, "eps must be finite and >= 0");
   const void* ptrs[9] = {r, k, v, w_raw, u, g, gamma, beta, out};
   const char* names[9] = {"r", "k", "v", "w_raw", "u", "g", "gamma", "beta", "out"};
   for (int i = 0; i < 9; ++i)
