@@ -79,3 +79,29 @@ def test_bf16_workload_values_are_representable():
     for key in ("r", "k", "v", "w_raw"):
         assert not np.any(x[key].view(np.uint32) & 0xFFFF)
     assert x["u"].dtype == np.float32
+
+
+def test_rwkv5_inputs():
+    a = I.random_inputs_wkv5(2, 7, 128, seed=5, dtype="bf16", wraw_lo=-4.0, wraw_hi=-1.0)
+    b = I.random_inputs_wkv5(2, 7, 128, seed=5, dtype="bf16", wraw_lo=-4.0, wraw_hi=-1.0)
+    assert a["w_raw"].shape == (128,) and a["r"].shape == (2, 7, 128) and a["u"].shape == (128,)
+    for key in ("r", "k", "v", "w_raw", "u"):
+        np.testing.assert_array_equal(a[key], b[key])
+    for key in ("r", "k", "v", "w_raw"):   # bf16-exact; u stays float32
+        assert not np.any(a[key].view(np.uint32) & 0xFFFF)
+    assert np.all((a["w_raw"] >= -4.0) & (a["w_raw"] <= -1.0))
+    with pytest.raises(ValueError):
+        I.random_inputs_wkv5(1, 2, 64, seed=0, dtype="f16")
+
+
+def test_rwkv4_inputs():
+    x = I.random_inputs_wkv4(3, 50, 40, seed=6, dtype="bf16", kscale=2.0, w_lo=0.5, w_hi=1.5)
+    assert x["k"].shape == x["v"].shape == (3, 50, 40) and x["w"].shape == x["u"].shape == (40,)
+    for key in ("k", "v"):
+        assert not np.any(x[key].view(np.uint32) & 0xFFFF)
+    assert np.any(x["w"].view(np.uint32) & 0xFFFF)   # w and u stay float32
+    assert np.all((x["w"] >= 0.5) & (x["w"] <= 1.5))
+    y = I.random_inputs_wkv4(3, 50, 40, seed=6, dtype="f32", kscale=2.0)
+    assert 1.7 < float(np.std(y["k"])) < 2.3
+    with pytest.raises(ValueError):
+        I.random_inputs_wkv4(1, 2, 8, seed=0, dtype="int8")
