@@ -1346,6 +1346,170 @@ __global__ __launch_bounds__(NT, 2) void summary_fixup_kernel(Params p) {
     sweep<BF16, false, kState, false, true, WS>(p, lds, bh, seg);
 }
 
+// Both directions' summaries of one segment of a bidirectional call in one
+// pass over its chunks in token order (fast path only: false at the first
+// chunk that needs the slow path).
+//   forward:  the state the causal sweep leaves, S <- 2^Ltot (S + (k 2^-Lin)^T V)
+//             per chunk, exactly as sweep() computes it;
+//   reverse:  the sweep from the segment's last token down leaves
+//             sum_i 2^(E_i) k_i^T v_i, with E_i the log2 decay of the segment's
+//             tokens before token i.  No term depends on another, so this sum
+//             accumulates in the same pass, with keys k 2^(P + Lex) (P: the
+//             decay of the segment's earlier chunks, Lex: the exclusive prefix
+//             inside the chunk), every factor at most 1.
+// Both share the loads, the scan and the value operands of each chunk.  The
+// reverse keys take the place of the state planes and P that of the bonus
+// row, neither of which a summary uses.
+template <bool BF16, bool WS>
+__device__ __forceinline__ bool summary_both(const Params& p, char* lds, int bh, int seg) {
+  constexpr int SP = BF16 ? 2 : 3;
+  constexpr int SV = BF16 ? 1 : 3;
+  using L = SweepLds<BF16>;
+  __bf16* sK = reinterpret_cast<__bf16*>(lds + L::kK);
+  __bf16* sV = reinterpret_cast<__bf16*>(lds + L::kV);
+  __bf16* sKr = reinterpret_cast<__bf16*>(lds + L::kS);
+  float* sBT = reinterpret_cast<float*>(lds + L::kBT);
+  float* sP = reinterpret_cast<float*>(lds + L::kU);
+  int* sFlag = reinterpret_cast<int*>(lds + L::kFlag);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int J = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  const int tau = 16 * J + li;
+  const LdsOff lo = lds_offsets(J, g, li);
+  const int b = bh / p.H, h = bh % p.H;
+  const int64_t T = p.T, C = p.C;
+  const int64_t base = (int64_t)b * T * C + (int64_t)h * HS;
+  const int64_t t_lo = (int64_t)seg * p.SEGC * LC;
+  const int64_t n = min(T, t_lo + (int64_t)p.SEGC * LC) - t_lo;
+  const int nch = (int)((n + LC - 1) / LC);
+  const int Ci = (int)C;
+  if (tid < 64) sP[tid] = 0.f;   // read after the first barrier
+
+  f32x4 S[4], R[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    R[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float gsum[4] = {0.f, 0.f, 0.f, 0.f};
+
+  constexpr int ISZ = BF16 ? 2 : 4;
+  const Rsrc rk = slice_rsrc(p.k, base, ISZ, T, C), rv = slice_rsrc(p.v, base, ISZ, T, C);
+  const Rsrc rw = WS ? slice_rsrc(p.w, (int64_t)h * HS, ISZ, 1, C) : slice_rsrc(p.w, base, ISZ, T, C);
+  const int in_row0 = (int)(t_lo + tau) * Ci * ISZ, in_step = LC * Ci * ISZ;
+  Raw<BF16> buf[3];   // k, v, w rows of the lane's token
+  auto fetch = [&](int ch) {
+    const bool in_seg = tau < (int)min<int64_t>(LC, n - (int64_t)ch * LC);
+    const int row = in_row0 + ch * in_step;
+    const int off = in_seg ? row : kOffNone;
+    buf[0] = gload<BF16>(rk, off, g);
+    buf[1] = gload<BF16>(rv, off, g);
+    buf[2] = gload<BF16>(rw, in_seg ? (WS ? 0 : row) : kOffNone, g);
+  };
+  fetch(0);
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int Lv = (int)min<int64_t>(LC, n - (int64_t)ch * LC);
+    const bool valid = tau < Lv;
+    const bool active = 16 * J < Lv;   // uniform in the wave
+    progress_priority(ch, nch);
+    lds_barrier();
+
+    // ---- phase A: in-block scan, block totals, values
+    float lin[2][8];
+    if (active) {
+      block_scan<BF16>(buf[2], valid ? -kLog2e : 0.f, lin);
+      publish_block(lin, sBT, sFlag, J, g, li, lane);
+      write_vT<BF16>(sV, lo.c, buf[1]);
+    } else {
+      publish_empty_block(sBT, sFlag, J, lane);
+      zero_cols16<SV>(sV, 16 * J, lane);
+      zero_rows16<SP>(sK, 16 * J, lane);
+      zero_rows16<SP>(sKr, 16 * J, lane);
+    }
+    lds_barrier();
+    if (chunk_is_slow(sFlag)) return false;   // uniform: every wave reads the same flags
+
+    // ---- phase B: forward keys k 2^(-Lin), reverse keys k 2^(P + Lex)
+    if (active) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int cb = 32 * ks + 8 * g;
+        float off[8], k[8], pr[8], kf[8], kr[8];
+        block_offset(sBT, J, cb, off);
+        unpack_half<BF16>(buf[0], ks, k);
+        load8f(&sP[cb], pr);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          kf[j] = k[j] * ex2(-(lin[ks][j] + off[j]));
+          kr[j] = k[j] * ex2(pr[j] + (row_shr<1>(lin[ks][j]) + off[j]));
+        }
+        wr8<SP>(sK, 1024 * J + lo.a[ks], kf);
+        wr8<SP>(sKr, 1024 * J + lo.a[ks], kr);
+      }
+    }
+    if (ch + 1 < nch) fetch(ch + 1);
+    lds_barrier();   // keys written; every wave has read P for this chunk
+
+    // ---- phase D: both states, rows 16J + 4g + j
+    float tot4[4], dec[4];
+    chunk_total4(sBT, 16 * J + 4 * g, tot4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dec[j] = ex2(tot4[j]);
+      gsum[j] += tot4[j];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (32 * ks >= Lv) break;
+      const Op<SP> key = rdcol8<SP>(sK, lo.kt, 2048 * ks);
+      const Op<SP> keyr = rdcol8<SP>(sKr, lo.kt, 2048 * ks);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const Op<SV> val = rd8<SV>(sV, 1024 * nt + lo.a[ks]);
+        S[nt] = mma(key, val, S[nt]);
+        R[nt] = mma(keyr, val, R[nt]);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[nt][j] *= dec[j];
+    // P of the next chunk (read there after two barriers)
+    if (li == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sP[16 * J + 4 * g + j] += tot4[j];
+    }
+  }
+
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    float* dst = p.summ + (((int64_t)bh * p.G + seg) * 2 + d) * kSummFloats;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const f32x4 x = d == 0 ? S[nt] : R[nt];
+      *reinterpret_cast<float4*>(dst + (16 * nt + li) * HS + 16 * J + 4 * g) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+    if (li == 0)
+      *reinterpret_cast<float4*>(dst + PL + 16 * J + 4 * g) = make_float4(gsum[0], gsum[1], gsum[2], gsum[3]);
+  }
+  return true;
+}
+
+// Summaries of bidirectional calls, both directions per workgroup; a segment
+// with a slow chunk marks both, and the fix-up kernel recomputes them.
+template <bool BF16, bool WS>
+__global__ __launch_bounds__(NT, occupancy<BF16>()) void summary_both_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
+  const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
+  if (!summary_both<BF16, WS>(p, lds, bh, seg)) {
+    set_marker(summary_marker(p, bh, seg, 0));
+    if (threadIdx.x == 0) *reinterpret_cast<uint32_t*>(summary_marker(p, bh, seg, 1)) = kRedo;
+  }
+}
+
 // State passing through an empty sequence: s_out = s_in (zero without s_in).
 __global__ __launch_bounds__(NT) void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                                        int64_t n) {
@@ -1527,7 +1691,10 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   hipError_t e;
   if (pl.G > 1) {
     const dim3 grid(bh * pl.G * (BIDIR ? 2 : 1));
-    hipLaunchKernelGGL((summary_kernel<BF16, BIDIR, WS>), grid, block, 0, s, p);
+    if constexpr (BIDIR)
+      hipLaunchKernelGGL((summary_both_kernel<BF16, WS>), dim3(bh * pl.G), block, 0, s, p);
+    else
+      hipLaunchKernelGGL((summary_kernel<BF16, BIDIR, WS>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((summary_fixup_kernel<BF16, BIDIR, WS>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
