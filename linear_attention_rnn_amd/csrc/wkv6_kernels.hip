@@ -1246,12 +1246,13 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 // forward sweep (it adds its part to y) in the same workgroup, so the partial
 // rows are read back from the L2 of the same XCD.
 //
-// Every item first runs with the fast path alone (wkv_kernel,
-// summary_kernel), register-allocated for three resident workgroups per CU.
-// A workgroup that meets a chunk needing the slow path stops and leaves a
-// marker in the first word of its output (y at the segment's first token and
-// the head's first channel, or g[0] of its summary); the fix-up kernel
-// launched next recomputes exactly the marked items with the general sweeps.
+// Every item first runs with the fast path alone (wkv_kernel),
+// register-allocated for three resident workgroups per CU.  A workgroup that
+// meets a chunk needing the slow path stops and leaves a marker in the first
+// word of its output (y at the segment's first token and the head's first
+// channel); the fix-up kernel launched next recomputes exactly the marked
+// items with the general sweeps, which need more registers than the fast
+// kernel has.  (The summary kernels need no such split: see there.)
 // A marker bit pattern produced by the arithmetic itself (a NaN input that
 // propagates there) only costs a needless recomputation.
 constexpr uint32_t kRedo = 0x7FC0D1A5u;   // quiet NaN with a payload
@@ -1266,10 +1267,6 @@ __device__ __forceinline__ float* item_marker(const Params& p, int bh, int seg) 
   if constexpr (EPI) return p.mark + (int64_t)bh * p.G + seg;   // the fused epilogue writes no y
   const int b = bh / p.H, h = bh % p.H;
   return p.y + ((int64_t)b * p.T + (int64_t)seg * p.SEGC * LC) * p.C + (int64_t)h * HS;
-}
-
-__device__ __forceinline__ float* summary_marker(const Params& p, int bh, int seg, int rev) {
-  return p.summ + (((int64_t)bh * p.G + seg) * 2 + rev) * kSummFloats + PL;
 }
 
 __device__ __forceinline__ void set_marker(float* m) {
@@ -1312,38 +1309,20 @@ __global__ __launch_bounds__(NT, 2) void wkv_fixup_kernel(Params p) {
   run_item<BF16, BIDIR, CARRY, true, WS, EPI>(p, lds, bh, seg);
 }
 
-// Segment summaries: end state and total decay of each segment in each sweep
-// direction, from a zero state (only those another segment needs).
-template <bool BF16, bool BIDIR>
-__device__ __forceinline__ bool summary_item(int& bh, int& seg, int& rev, const Params& p) {
-  const int dirs = BIDIR ? 2 : 1;
-  bh = blockIdx.x / (p.G * dirs);
-  const int rem = blockIdx.x % (p.G * dirs);
-  seg = rem / dirs;
-  rev = rem % dirs;
-  return rev ? seg > 0 : seg < p.G - 1;
-}
-
-template <bool BF16, bool BIDIR, bool WS>
+// Segment summaries of causal calls: the forward sweep's end state and total
+// log2 decay of every segment but the last, from a zero state.  A segment
+// with a chunk that needs the slow path is recomputed at once with the
+// general sweep: without outputs it fits the same register budget, so no
+// fix-up launch is needed.
+template <bool BF16, bool WS>
 __global__ __launch_bounds__(NT, occupancy<BF16>()) void summary_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
-  int bh, seg, rev;
-  if (!summary_item<BF16, BIDIR>(bh, seg, rev, p)) return;
-  const bool ok = rev ? sweep<BF16, true, kState, false, false, WS>(p, lds, bh, seg)
-                      : sweep<BF16, false, kState, false, false, WS>(p, lds, bh, seg);
-  if (!ok) set_marker(summary_marker(p, bh, seg, rev));
-}
-
-template <bool BF16, bool BIDIR, bool WS>
-__global__ __launch_bounds__(NT, 2) void summary_fixup_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
-  int bh, seg, rev;
-  if (!summary_item<BF16, BIDIR>(bh, seg, rev, p)) return;
-  if (!marker_set(summary_marker(p, bh, seg, rev))) return;
-  if (rev)
-    sweep<BF16, true, kState, false, true, WS>(p, lds, bh, seg);
-  else
+  const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
+  if (seg == p.G - 1) return;   // no later segment needs it
+  if (!sweep<BF16, false, kState, false, false, WS>(p, lds, bh, seg)) {
+    __syncthreads();   // every wave is done with the fast attempt's LDS
     sweep<BF16, false, kState, false, true, WS>(p, lds, bh, seg);
+  }
 }
 
 // Both directions' summaries of one segment of a bidirectional call in one
@@ -1498,15 +1477,19 @@ __device__ __forceinline__ bool summary_both(const Params& p, char* lds, int bh,
   return true;
 }
 
-// Summaries of bidirectional calls, both directions per workgroup; a segment
-// with a slow chunk marks both, and the fix-up kernel recomputes them.
+// Summaries of bidirectional calls, both directions per workgroup.  A
+// segment with a chunk that needs the slow path is recomputed at once with
+// the general sweeps, one direction after the other (the forward summary of
+// the last segment and the reverse one of the first are never read).
 template <bool BF16, bool WS>
 __global__ __launch_bounds__(NT, occupancy<BF16>()) void summary_both_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[SweepLds<BF16>::kBytes];
   const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
   if (!summary_both<BF16, WS>(p, lds, bh, seg)) {
-    set_marker(summary_marker(p, bh, seg, 0));
-    if (threadIdx.x == 0) *reinterpret_cast<uint32_t*>(summary_marker(p, bh, seg, 1)) = kRedo;
+    __syncthreads();   // every wave is done with the fast attempt's LDS
+    if (seg < p.G - 1) sweep<BF16, false, kState, false, true, WS>(p, lds, bh, seg);
+    __syncthreads();
+    if (seg > 0) sweep<BF16, true, kState, false, true, WS>(p, lds, bh, seg);
   }
 }
 
@@ -1690,13 +1673,11 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   const dim3 block(NT);
   hipError_t e;
   if (pl.G > 1) {
-    const dim3 grid(bh * pl.G * (BIDIR ? 2 : 1));
+    const dim3 sgrid(bh * pl.G);
     if constexpr (BIDIR)
-      hipLaunchKernelGGL((summary_both_kernel<BF16, WS>), dim3(bh * pl.G), block, 0, s, p);
+      hipLaunchKernelGGL((summary_both_kernel<BF16, WS>), sgrid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((summary_kernel<BF16, BIDIR, WS>), grid, block, 0, s, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((summary_fixup_kernel<BF16, BIDIR, WS>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((summary_kernel<BF16, WS>), sgrid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 grid(bh * pl.G);
