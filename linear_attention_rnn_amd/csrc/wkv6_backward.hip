@@ -189,6 +189,12 @@ struct Smem {
   float ov[TB][NT / 64][HS];          // per token and wave: partial column sums for dv
 };
 
+// Decay of a staged value: lambda = -exp(w_raw), w = exp(lambda).
+__device__ __forceinline__ void decay4(float4 wr, float4& lam, float4& w) {
+  lam = make_float4(-ex2(wr.x * kLog2e), -ex2(wr.y * kLog2e), -ex2(wr.z * kLog2e), -ex2(wr.w * kLog2e));
+  w = make_float4(ex2(lam.x * kLog2e), ex2(lam.y * kLog2e), ex2(lam.z * kLog2e), ex2(lam.w * kLog2e));
+}
+
 // One thread's share of a block as loaded from HBM (zeros past the end).
 template <bool BF16>
 struct Pre {
@@ -197,10 +203,9 @@ struct Pre {
 };
 
 // REV: the later-token part of a bidirectional call (reversed token order,
-// no u term, outputs accumulated).  SUM: a segment's summaries only (its
-// state from zero, its adjoint from zero, its total log decay) for the carry
-// kernel.  One workgroup per (batch item, head, segment).
-template <bool BF16, bool REV, bool SUM>
+// no u term, outputs accumulated).  One workgroup per (batch item, head,
+// segment); the segments of a segmented call start from the carries.
+template <bool BF16, bool REV>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   __shared__ Smem sm;
   const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
@@ -230,11 +235,6 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   for (int i = 0; i < 4; ++i) uc[i] = REV ? 0.f : p.u[h * HS + cc + i];
   float* drw = REV ? p.dr_tmp : p.dr;   // where pass 1 leaves dr
 
-  // decay of a staged value: lambda = -exp(w_raw), w = exp(lambda)
-  auto decay = [](float4 wr, float4& lam, float4& w) {
-    lam = make_float4(-ex2(wr.x * kLog2e), -ex2(wr.y * kLog2e), -ex2(wr.z * kLog2e), -ex2(wr.w * kLog2e));
-    w = make_float4(ex2(lam.x * kLog2e), ex2(lam.y * kLog2e), ex2(lam.z * kLog2e), ex2(lam.w * kLog2e));
-  };
   // Every prefetch reads a valid row: positions past the end repeat the last
   // token and staging zeroes them, so the loads need no branch (a branch
   // would make the compiler wait for them at once).
@@ -243,27 +243,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     const int64_t q = pos(bi);
     return row_of(q < q1 ? q : q1 - 1) + cc;
   };
-  // SUM: the segment's total log decay, per staged channel (summed over the
-  // staged tokens, then over the workgroup at the end)
-  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-  auto add_lam = [&](bool ok, float4 lam) {
-    if (ok) {
-      lsum[0] += lam.x;
-      lsum[1] += lam.y;
-      lsum[2] += lam.z;
-      lsum[3] += lam.w;
-    }
-  };
-  const bool run_fwd = !SUM || seg < p.G - 1;   // summaries: the state of every segment but the last,
-  const bool run_bwd = !SUM || seg > 0;         // the adjoint of every segment but the first
-  const bool lam_in_fwd = run_fwd;              // the pass that also sums the decay
   auto stage_dyv = [&](float4 dy, float4 v) {
     const float d = row_sum(fmaf(dy.x, v.x, fmaf(dy.y, v.y, fmaf(dy.z, v.z, dy.w * v.w))));
     if (cc == 0) sm.dyv[ts] = d;
   };
 
   // ---------------- pass 1: forward sweep, state S, dr
-  if (run_fwd) {
+  {
     Pre<BF16> x;
     float4 old_dr;   // REV: the causal part already in p.dr, for the block whose dr leaves next
     auto load = [&](int bi) {
@@ -271,7 +257,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       x.k = ld4<BF16>(p.k, o);
       x.w = ld4<BF16>(p.w, o);
       x.v = ld4<BF16>(p.v, o);
-      if (!SUM) x.dy = f4(p.dy + o);
+      x.dy = f4(p.dy + o);
     };
     auto out = [&](int bi) {   // dr of block bi: staged partial sums plus u k (dy . v)
       const int64_t q = pos(bi);
@@ -289,7 +275,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) S[i][j] = 0.f;
-    if (!SUM && segmented) {   // the state the earlier segments hand over
+    if (segmented) {   // the state the earlier segments hand over
       const float* si = p.Sin + ((int64_t)bh * p.G + seg) * (HS * HS);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -303,25 +289,21 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     load(0);
     for (int bi = 0; bi < nblk; ++bi) {
       __syncthreads();   // the previous block's token steps are done with the staging arrays
-      if (!SUM && bi > 0) out(bi - 1);
+      if (bi > 0) out(bi - 1);
       {
         const bool ok = pos(bi) < q1;
         const float4 k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v));
         float4 lam, w;
-        decay(widen(x.w), lam, w);
+        decay4(widen(x.w), lam, w);
         st4(&sm.k[ts][cc], k);
         st4(&sm.w[ts][cc], w);
         st4(&sm.v[ts][cc], v);
-        if (SUM) {
-          add_lam(ok, lam);
-        } else {
-          const float4 dy = keep(ok, x.dy);
-          st4(&sm.dy[ts][cc], dy);
-          stage_dyv(dy, v);
-        }
+        const float4 dy = keep(ok, x.dy);
+        st4(&sm.dy[ts][cc], dy);
+        stage_dyv(dy, v);
       }
       __syncthreads();
-      if (REV && !SUM) old_dr = f4(p.dr + at_q(bi));
+      if (REV) old_dr = f4(p.dr + at_q(bi));
       load(bi + 1 < nblk ? bi + 1 : bi);
       struct Tk {
         float4 k, w, v, dy;
@@ -331,7 +313,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         e.k = f4(&sm.k[tt][c0]);
         e.w = f4(&sm.w[tt][c0]);
         e.v = f4(&sm.v[tt][n0]);
-        if (!SUM) e.dy = f4(&sm.dy[tt][n0]);
+        e.dy = f4(&sm.dy[tt][n0]);
         return e;
       };
       Tk nx = rd(0);
@@ -339,7 +321,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       for (int tt = 0; tt < TB; ++tt) {
         const Tk e = nx;
         if (tt + 1 < TB) nx = rd(tt + 1);   // the next token's operands are in flight during this one
-        if (!SUM) {
+        {
           float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -356,19 +338,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
       }
     }
-    if (SUM) {
-      float* so = p.Sl + ((int64_t)bh * p.G + seg) * (HS * HS);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st4(so + (c0 + i) * HS + n0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
-    } else {
-      __syncthreads();
-      out(nblk - 1);
-    }
+    __syncthreads();
+    out(nblk - 1);
   }
   __syncthreads();   // pass 1's dr rows are written before pass 2 reads them
 
   // ---------------- pass 2: backward sweep, adjoint G, dk, dv, dw_raw
-  if (run_bwd) {
+  {
     Pre<BF16> x;
     float4 old_k, old_v, old_w;   // REV: the causal parts already in the outputs, for the block that leaves next
     auto load = [&](int bi) {
@@ -376,11 +352,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       x.r = ld4<BF16>(p.r, o);
       x.w = ld4<BF16>(p.w, o);
       x.dy = f4(p.dy + o);
-      if (!SUM) {
-        x.k = ld4<BF16>(p.k, o);
-        x.v = ld4<BF16>(p.v, o);
-        x.dr = f4(drw + o);
-      }
+      x.k = ld4<BF16>(p.k, o);
+      x.v = ld4<BF16>(p.v, o);
+      x.dr = f4(drw + o);
     };
     auto load_old = [&](int bi) {
       const int64_t o = at_q(bi);
@@ -423,7 +397,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) G[i][j] = 0.f;
-    if (!SUM && segmented) {   // the adjoint the later segments hand back
+    if (segmented) {   // the adjoint the later segments hand back
       const float* gi = p.Gin + ((int64_t)bh * p.G + seg) * (HS * HS);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -440,28 +414,24 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
     load(nblk - 1);
     for (int bi = nblk - 1; bi >= 0; --bi) {
       __syncthreads();   // the previous block's token steps are done with the staging arrays
-      if (!SUM && bi < nblk - 1) out(bi + 1);
+      if (bi < nblk - 1) out(bi + 1);
       {
         const bool ok = pos(bi) < q1;
         const float4 r = keep(ok, widen(x.r)), dy = keep(ok, x.dy);
         float4 lam, w;
-        decay(widen(x.w), lam, w);
+        decay4(widen(x.w), lam, w);
         st4(&sm.r[ts][cc], r);
         st4(&sm.w[ts][cc], w);
         st4(&sm.dy[ts][cc], dy);
-        if (SUM) {
-          if (!lam_in_fwd) add_lam(ok, lam);
-        } else {
-          const float4 k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v)), dr = keep(ok, x.dr);
-          st4(&sm.k[ts][cc], k);
-          st4(&sm.lam[ts][cc], lam);
-          st4(&sm.x[ts][cc], make_float4(r.x * dr.x, r.y * dr.y, r.z * dr.z, r.w * dr.w));
-          st4(&sm.v[ts][cc], v);
-          stage_dyv(dy, v);
-        }
+        const float4 k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v)), dr = keep(ok, x.dr);
+        st4(&sm.k[ts][cc], k);
+        st4(&sm.lam[ts][cc], lam);
+        st4(&sm.x[ts][cc], make_float4(r.x * dr.x, r.y * dr.y, r.z * dr.z, r.w * dr.w));
+        st4(&sm.v[ts][cc], v);
+        stage_dyv(dy, v);
       }
       __syncthreads();
-      if (REV && !SUM) load_old(bi);
+      if (REV) load_old(bi);
       load(bi > 0 ? bi - 1 : 0);
       struct Tk {
         float4 r, k, w, v, dy;
@@ -472,14 +442,12 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         e.r = f4(&sm.r[tt][c0]);
         e.w = f4(&sm.w[tt][c0]);
         e.dy = f4(&sm.dy[tt][n0]);
-        if (!SUM) {
-          e.k = f4(&sm.k[tt][c0]);
-          e.v = f4(&sm.v[tt][n0]);
-          e.d = sm.dyv[tt];
-          e.ki = sm.k[tt][c0 + ri];
-          e.rdri = sm.x[tt][c0 + ri];
-          e.rui = sm.r[tt][c0 + ri] * u_ri;
-        }
+        e.k = f4(&sm.k[tt][c0]);
+        e.v = f4(&sm.v[tt][n0]);
+        e.d = sm.dyv[tt];
+        e.ki = sm.k[tt][c0 + ri];
+        e.rdri = sm.x[tt][c0 + ri];
+        e.rui = sm.r[tt][c0 + ri] * u_ri;
         return e;
       };
       Tk nx = rd(TB - 1);
@@ -487,7 +455,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       for (int tt = TB - 1; tt >= 0; --tt) {
         const Tk e = nx;
         if (tt > 0) nx = rd(tt - 1);   // the next token's operands are in flight during this one
-        if (!SUM) {
+        {
           float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -517,40 +485,155 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
       }
     }
-    if (SUM) {
-      float* go = p.Gl + ((int64_t)bh * p.G + seg) * (HS * HS);
+    __syncthreads();
+    out(0);
+    // the segment's sum of r dr - k dk: D at its first token plus that token's r dr
+    if (segmented && (lane & 3) == 0) p.sig[((int64_t)bh * p.G + seg) * HS + c0 + ri] = (D - Dc) + rdr_next;
+    if (!REV) {   // du over the threads that share the channels: rows of the wave, then the waves
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st4(go + (c0 + i) * HS + n0, make_float4(G[i][0], G[i][1], G[i][2], G[i][3]));
-    } else {
+      for (int i = 0; i < 4; ++i) du[i] = rows_sum(du[i]);
       __syncthreads();
-      out(0);
-      // the segment's sum of r dr - k dk: D at its first token plus that token's r dr
-      if (segmented && (lane & 3) == 0) p.sig[((int64_t)bh * p.G + seg) * HS + c0 + ri] = (D - Dc) + rdr_next;
-      if (!REV) {   // du over the threads that share the channels: rows of the wave, then the waves
-#pragma unroll
-        for (int i = 0; i < 4; ++i) du[i] = rows_sum(du[i]);
-        __syncthreads();
-        if (lane < 16) st4(&sm.ov[0][wave][cc], make_float4(du[0], du[1], du[2], du[3]));
-        __syncthreads();
-        if (t < 16) {
-          const float4 s = add4(add4(f4(&sm.ov[0][0][cc]), f4(&sm.ov[0][1][cc])),
-                                add4(f4(&sm.ov[0][2][cc]), f4(&sm.ov[0][3][cc])));
-          st4(p.du_part + ((int64_t)b * p.G + seg) * C + h * HS + cc, s);
-        }
+      if (lane < 16) st4(&sm.ov[0][wave][cc], make_float4(du[0], du[1], du[2], du[3]));
+      __syncthreads();
+      if (t < 16) {
+        const float4 s = add4(add4(f4(&sm.ov[0][0][cc]), f4(&sm.ov[0][1][cc])),
+                              add4(f4(&sm.ov[0][2][cc]), f4(&sm.ov[0][3][cc])));
+        st4(p.du_part + ((int64_t)b * p.G + seg) * C + h * HS + cc, s);
       }
     }
   }
-  if (SUM) {   // the segment's total log decay per channel: over the staging rows, then the waves
+}
+
+// A segment's summaries for the carry kernel, in one pass over its sweep
+// positions in order (one workgroup per batch item, head and segment):
+//   Sl  its state after its last token, from zero: S <- w S + k^T v;
+//   Gl  its adjoint before its first token, from zero after its last:
+//       sum_q (prod of w over the segment's positions before q) r_q^T dy_q.
+//       No term of that sum depends on another, so it accumulates in the
+//       same pass as the state, with the running decay product P
+//       (P <- w P after each position, from 1);
+//   Wl  its total log decay, sum_q lambda_q, per channel.
+// The state of the last segment and the adjoint of the first are never read
+// and not stored.
+struct SummSmem {
+  float r[TB][HS], k[TB][HS], w[TB][HS], v[TB][HS], dy[TB][HS];
+  float red[NT / 64][HS];
+};
+
+template <bool BF16, bool REV>
+__global__ __launch_bounds__(NT) void bwd_summary_kernel(BwdParams p) {
+  __shared__ SummSmem sm;
+  const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
+  const int b = bh / p.H, h = bh % p.H;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // token steps: rows c0 .. c0 + 3 and columns n0 .. n0 + 3 of both summaries
+  const int c0 = 4 * (t >> 4), n0 = 4 * (t & 15);
+  // staging: token ts of the block, channels cc .. cc + 3
+  const int ts = t >> 4, cc = 4 * (t & 15);
+  const int64_t T = p.T, C = p.C;
+  const int64_t q0 = (int64_t)seg * p.SEGL, q1 = T < q0 + p.SEGL ? T : q0 + p.SEGL;
+  const int nblk = (int)((q1 - q0 + TB - 1) / TB);
+  const int64_t head = (int64_t)b * T * C + (int64_t)h * HS;
+  auto row_of = [&](int64_t q) { return head + (REV ? T - 1 - q : q) * C; };
+  auto pos = [&](int bi) { return q0 + (int64_t)bi * TB + ts; };
+  // positions past the end repeat the last token (staging zeroes them), so
+  // the prefetch needs no branch
+  auto at_q = [&](int bi) {
+    const int64_t q = pos(bi);
+    return row_of(q < q1 ? q : q1 - 1) + cc;
+  };
+
+  Pre<BF16> x;
+  auto load = [&](int bi) {
+    const int64_t o = at_q(bi);
+    x.r = ld4<BF16>(p.r, o);
+    x.k = ld4<BF16>(p.k, o);
+    x.w = ld4<BF16>(p.w, o);
+    x.v = ld4<BF16>(p.v, o);
+    x.dy = f4(p.dy + o);
+  };
+  float S[4][4], G[4][4], P[4] = {1.f, 1.f, 1.f, 1.f}, lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lsum[i] = rows_sum(lsum[i]);
-    __syncthreads();
-    if (lane < 16) st4(&sm.ov[0][wave][cc], make_float4(lsum[0], lsum[1], lsum[2], lsum[3]));
-    __syncthreads();
-    if (t < 16) {
-      const float4 s4 = add4(add4(f4(&sm.ov[0][0][cc]), f4(&sm.ov[0][1][cc])),
-                             add4(f4(&sm.ov[0][2][cc]), f4(&sm.ov[0][3][cc])));
-      st4(p.Wl + ((int64_t)bh * p.G + seg) * HS + cc, s4);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      S[i][j] = 0.f;
+      G[i][j] = 0.f;
     }
+  load(0);
+  for (int bi = 0; bi < nblk; ++bi) {
+    __syncthreads();   // the previous block's token steps are done with the staging arrays
+    {
+      // past the end: zero keys, values, queries and output gradients (their
+      // decays only touch summaries after the last real position)
+      const bool ok = pos(bi) < q1;
+      float4 lam, w;
+      decay4(widen(x.w), lam, w);
+      st4(&sm.r[ts][cc], keep(ok, widen(x.r)));
+      st4(&sm.k[ts][cc], keep(ok, widen(x.k)));
+      st4(&sm.w[ts][cc], w);
+      st4(&sm.v[ts][cc], keep(ok, widen(x.v)));
+      st4(&sm.dy[ts][cc], keep(ok, x.dy));
+      if (ok) {
+        lsum[0] += lam.x;
+        lsum[1] += lam.y;
+        lsum[2] += lam.z;
+        lsum[3] += lam.w;
+      }
+    }
+    __syncthreads();
+    load(bi + 1 < nblk ? bi + 1 : bi);
+    struct Tk {
+      float4 r, k, w, v, dy;
+    };
+    auto rd = [&](int tt) {
+      Tk e;
+      e.r = f4(&sm.r[tt][c0]);
+      e.k = f4(&sm.k[tt][c0]);
+      e.w = f4(&sm.w[tt][c0]);
+      e.v = f4(&sm.v[tt][n0]);
+      e.dy = f4(&sm.dy[tt][n0]);
+      return e;
+    };
+    Tk nx = rd(0);
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
+      const Tk e = nx;
+      if (tt + 1 < TB) nx = rd(tt + 1);   // the next token's operands are in flight during this one
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ki = at(e.k, i), wi = at(e.w, i), pr = P[i] * at(e.r, i);
+        S[i][0] = fmaf(wi, S[i][0], ki * e.v.x);
+        S[i][1] = fmaf(wi, S[i][1], ki * e.v.y);
+        S[i][2] = fmaf(wi, S[i][2], ki * e.v.z);
+        S[i][3] = fmaf(wi, S[i][3], ki * e.v.w);
+        G[i][0] = fmaf(pr, e.dy.x, G[i][0]);
+        G[i][1] = fmaf(pr, e.dy.y, G[i][1]);
+        G[i][2] = fmaf(pr, e.dy.z, G[i][2]);
+        G[i][3] = fmaf(pr, e.dy.w, G[i][3]);
+        P[i] *= wi;
+      }
+    }
+  }
+  const int64_t item = (int64_t)bh * p.G + seg;
+  if (seg < p.G - 1) {
+    float* so = p.Sl + item * (HS * HS);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st4(so + (c0 + i) * HS + n0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
+  }
+  if (seg > 0) {
+    float* go = p.Gl + item * (HS * HS);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st4(go + (c0 + i) * HS + n0, make_float4(G[i][0], G[i][1], G[i][2], G[i][3]));
+  }
+  // the total log decay per channel: over the staging rows, then the waves
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lsum[i] = rows_sum(lsum[i]);
+  if (lane < 16) st4(&sm.red[wave][cc], make_float4(lsum[0], lsum[1], lsum[2], lsum[3]));
+  __syncthreads();
+  if (t < 16) {
+    const float4 s4 = add4(add4(f4(&sm.red[0][cc]), f4(&sm.red[1][cc])), add4(f4(&sm.red[2][cc]), f4(&sm.red[3][cc])));
+    st4(p.Wl + item * HS + cc, s4);
   }
 }
 
@@ -754,23 +837,20 @@ void set_carries(BwdParams& p, char* ws, size_t off, int64_t bh, int G) {
   p.sig = f + 4 * st + vec;
 }
 
-template <bool BF16, bool REV, bool SUM>
-void launch_one(dim3 grid, hipStream_t s, const BwdParams& p) {
-  hipLaunchKernelGGL((bwd_kernel<BF16, REV, SUM>), grid, dim3(NT), 0, s, p);
+// sum: the segment summaries (bwd_summary_kernel), else the gradient passes.
+template <bool BF16, bool REV>
+void launch_one(bool sum, dim3 grid, hipStream_t s, const BwdParams& p) {
+  if (sum)
+    hipLaunchKernelGGL((bwd_summary_kernel<BF16, REV>), grid, dim3(NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_kernel<BF16, REV>), grid, dim3(NT), 0, s, p);
 }
 
 void launch_bwd(bool bf16, bool rev, bool sum, dim3 grid, hipStream_t s, const BwdParams& p) {
-  if (bf16) {
-    if (rev)
-      sum ? launch_one<true, true, true>(grid, s, p) : launch_one<true, true, false>(grid, s, p);
-    else
-      sum ? launch_one<true, false, true>(grid, s, p) : launch_one<true, false, false>(grid, s, p);
-  } else {
-    if (rev)
-      sum ? launch_one<false, true, true>(grid, s, p) : launch_one<false, true, false>(grid, s, p);
-    else
-      sum ? launch_one<false, false, true>(grid, s, p) : launch_one<false, false, false>(grid, s, p);
-  }
+  if (bf16)
+    rev ? launch_one<true, true>(sum, grid, s, p) : launch_one<true, false>(sum, grid, s, p);
+  else
+    rev ? launch_one<false, true>(sum, grid, s, p) : launch_one<false, false>(sum, grid, s, p);
 }
 
 }  // namespace

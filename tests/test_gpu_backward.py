@@ -122,3 +122,18 @@ def test_backward_segments(torch_cuda, monkeypatch, mode):
         for name in NAMES:
             scale = float(np.sqrt(np.mean(got[1][name] ** 2))) or 1.0
             assert float(np.max(np.abs(got[G][name] - got[1][name]))) / scale <= 1e-4, (G, name)
+
+
+@pytest.mark.parametrize("mode", ["causal", "bidirectional"])
+def test_backward_segments_decay_extremes(torch_cuda, monkeypatch, mode):
+    """Segment summaries under decays of 1 (w_raw = -inf), 0 to rounding
+    (w_raw = 1.5) and between, mixed per token and channel: the carried state,
+    adjoint and total decay still give the oracle's gradients."""
+    B, T, H = 1, 200, 2
+    x = I.random_inputs(B, T, 64 * H, H, seed=90, dtype="f32")
+    x["w_raw"] = np.random.default_rng(91).choice(
+        np.array([-np.inf, -20.0, -4.0, 0.0, 1.5], np.float32), size=x["w_raw"].shape)
+    dy = dy_of(x, 92)
+    for G in (1, 3):
+        monkeypatch.setenv("WKV6_BWD_SEGMENTS", str(G))
+        check(f"segments {G} extremes {mode}", x, dy, H, mode, "f32")
