@@ -91,12 +91,14 @@ hipError_t ws_alloc(void** p, size_t bytes, hipStream_t s) {
       props.allocType = hipMemAllocationTypePinned;
       props.location.type = hipMemLocationTypeDevice;
       props.location.id = dev;
-      if ((e = hipMemPoolCreate(&pools[dev], &props)) != hipSuccess) {
-        pools[dev] = nullptr;
+      hipMemPool_t created = nullptr;
+      if ((e = hipMemPoolCreate(&created, &props)) != hipSuccess) return e;
+      uint64_t keep = UINT64_MAX;
+      if ((e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
+        hipMemPoolDestroy(created);   // a pool that hands blocks back would cost every call an allocation
         return e;
       }
-      uint64_t keep = UINT64_MAX;
-      if ((e = hipMemPoolSetAttribute(pools[dev], hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) return e;
+      pools[dev] = created;
     }
     pool = pools[dev];
   }
