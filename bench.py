@@ -55,12 +55,15 @@ METRIC = "WKV6 fwd tokens/s (B·T/s) + % HBM roofline & MFMA util at N=64, 1 GPU
 
 
 def kernel_source_hash() -> str:
-    """Hash of the library sources with comments and blank lines stripped, so
-    that a recorded counter run stays matched to the code it measured."""
+    """Hash of the kernel sources (the .hip files and the header they share)
+    with comments and blank lines stripped, so that a recorded counter run
+    stays matched to the kernels it measured; host-only code is left out."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_rnn_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
