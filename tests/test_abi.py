@@ -57,6 +57,30 @@ def test_rejects_bad_arguments(kw, status):
     assert wkv6.last_error() != ""
 
 
+def test_last_error_is_per_thread():
+    """Two host threads fail in different ways at the same time; each then
+    reads the detail of its own call (the library's one piece of state is
+    kept per thread)."""
+    import threading
+
+    both_failed = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, kw):
+        status = _call(**kw)
+        both_failed.wait()   # neither reads its message before both calls have failed
+        seen[name] = (status, wkv6.last_error())
+
+    threads = [threading.Thread(target=worker, args=("mode", dict(mode=2))),
+               threading.Thread(target=worker, args=("head", dict(C=96, H=2)))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=30)
+    assert seen["mode"][0] == wkv6.ERR_INVALID_ARG and "mode" in seen["mode"][1]
+    assert seen["head"][0] == wkv6.ERR_UNSUPPORTED and "head size" in seen["head"][1]
+
+
 def test_empty_problem_is_a_noop():
     assert _call(B=0, ptrs=[0] * 6) == wkv6.OK
     assert _call(T=0, ptrs=[0] * 6) == wkv6.OK

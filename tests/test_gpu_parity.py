@@ -150,6 +150,45 @@ def test_runs_on_a_side_stream(torch_cuda):
     assert err_over_rms(y.double().cpu().numpy(), y_ref) <= TOL["f32"]
 
 
+def test_concurrent_host_threads(torch_cuda):
+    """Four host threads call the library at once, each on its own stream with
+    its own inputs, in calls that take a workspace from the shared per-device
+    pool (two items only, so the sequences are cut into segments).  Every
+    result equals the same call made alone, bit for bit."""
+    torch = torch_cuda
+    import threading
+    from linear_attention_rnn_amd import wkv6
+
+    B, T, H = 1, 64 * 6 + 7, 2
+    ds = [device_inputs(I.random_inputs(B, T, 64 * H, H, seed=300 + i, dtype="bf16"), "bf16")
+          for i in range(4)]
+    alone = [wkv6.fwd(*d, H, "bidirectional") for d in ds]
+    torch.cuda.synchronize()
+    results, errors = [None] * 4, []
+    start = threading.Barrier(4)
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            start.wait()
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    y = wkv6.fwd(*ds[i], H, "bidirectional", stream=s)
+            s.synchronize()
+            results[i] = y
+        except Exception as e:   # reported below, on the test's thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    for i in range(4):
+        assert results[i] is not None and torch.equal(results[i], alone[i]), i
+
+
 def test_empty_problem_on_gpu(torch_cuda):
     torch = torch_cuda
     from linear_attention_rnn_amd import wkv6
