@@ -985,19 +985,27 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
   const Rsrc rg = FIN ? slice_rsrc(p.gate, base, ISZ, T, C) : Rsrc();
   const Rsrc ro = FIN ? slice_rsrc(p.out, base, 2, T, C) : Rsrc();
   Raw<BF16> buf[4];
-  const int in_row0 = tok0 * Ci * ISZ, in_step = dir_rows * LC * Ci * ISZ;
-  const int y_row0 = tok0 * Ci * 4 + 16 * g, y_step = dir_rows * LC * Ci * 4;
-  const int g_row0 = in_row0 + 4 * g * ISZ;                                   // fused epilogue: gate rows
-  const int o_row0 = tok0 * Ci * 2 + 8 * g, o_step = dir_rows * LC * Ci * 2;   // and bf16 output rows
+  // Byte offsets are formed in unsigned 32-bit arithmetic: a lane past the
+  // segment's end may address up to 63 rows beyond the slice, past 2^31 at
+  // the largest accepted T; such lanes use kOffNone instead, and every real
+  // row's offset is below 2^31.
+  const uint32_t utok = (uint32_t)tok0, uC = (uint32_t)Ci, udir = (uint32_t)dir_rows;
+  const uint32_t in_row0 = utok * uC * ISZ, in_step = udir * LC * uC * ISZ;
+  const uint32_t y_row0 = utok * uC * 4 + 16 * g, y_step = udir * LC * uC * 4;
+  const uint32_t g_row0 = in_row0 + 4 * g * ISZ;                             // fused epilogue: gate rows
+  const uint32_t o_row0 = utok * uC * 2 + 8 * g, o_step = udir * LC * uC * 2;   // and bf16 output rows
+  // the offset of the lane's row in chunk ch, or kOffNone for a lane past the end
+  auto at = [](bool ok, uint32_t row0, uint32_t step, int ch) {
+    return ok ? (int)(row0 + (uint32_t)ch * step) : kOffNone;
+  };
   auto fetch = [&](int ch) {
     // tokens past the segment read zero
     const bool in_seg = tau < (int)min<int64_t>(LC, n - (int64_t)ch * LC);
-    const int row = in_row0 + ch * in_step;
-    const int off = in_seg ? row : kOffNone;
+    const int off = at(in_seg, in_row0, in_step, ch);
     if (OUT) buf[0] = gload<BF16>(rr, off, g);
     buf[1] = gload<BF16>(rk, off, g);
     buf[2] = gload<BF16>(rv, off, g);
-    buf[3] = gload<BF16>(rw, in_seg ? (WS ? 0 : row) : kOffNone, g);
+    buf[3] = gload<BF16>(rw, WS ? (in_seg ? 0 : kOffNone) : off, g);
   };
   fetch(0);
 
@@ -1035,7 +1043,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // byte offset of the lane's output row; lanes past the segment get an
     // offset outside every slice, so their loads read zero and their stores
     // are dropped without a branch
-    const int yoff = valid ? y_row0 + ch * y_step : kOffNone;
+    const int yoff = at(valid, y_row0, y_step, ch);
     f32x4 Y[4];
     GateRaw<BF16> gt;
     if (OUT && active) {
@@ -1080,7 +1088,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // outputs
     if (OUT && active) {
       // the gate rows for the fused epilogue, in flight during the products
-      if (FIN) gt = load_gate<BF16>(rg, valid ? g_row0 + ch * in_step : kOffNone);
+      if (FIN) gt = load_gate<BF16>(rg, at(valid, g_row0, in_step, ch));
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         const int I0 = 2 * pr;
@@ -1115,7 +1123,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
           for (int nt = 0; nt < 4; ++nt) Y[nt] = mma(rd8<SP>(sS, 1024 * nt + lo.a[ks]), q[ks], Y[nt]);
       }
       if constexpr (FIN) {
-        gn_gate_store<BF16>(Y, gt, sGm, sGm + 64, g, p.eps, ro, valid ? o_row0 + ch * o_step : kOffNone);
+        gn_gate_store<BF16>(Y, gt, sGm, sGm + 64, g, p.eps, ro, at(valid, o_row0, o_step, ch));
       } else {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) bstoref4(ry, yoff + 64 * nt, Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
@@ -1181,9 +1189,9 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
       lds_barrier();
 
       slow_chunk<BF16, MODE, DIAG, FIN>(p, lds, buf[0], buf[1], buf[3], ry,
-                                        valid ? y_row0 + ch * y_step : kOffNone, Lv, left, rg,
-                                        valid ? g_row0 + ch * in_step : kOffNone, ro,
-                                        valid ? o_row0 + ch * o_step : kOffNone);
+                                        at(valid, y_row0, y_step, ch), Lv, left, rg,
+                                        at(valid, g_row0, in_step, ch), ro,
+                                        at(valid, o_row0, o_step, ch));
       if (ch == nch - 1) {
         if (OUT && !keep_state) break;
       } else {
@@ -1377,15 +1385,15 @@ __device__ __forceinline__ bool summary_both(const Params& p, char* lds, int bh,
   constexpr int ISZ = BF16 ? 2 : 4;
   const Rsrc rk = slice_rsrc(p.k, base, ISZ, T, C), rv = slice_rsrc(p.v, base, ISZ, T, C);
   const Rsrc rw = WS ? slice_rsrc(p.w, (int64_t)h * HS, ISZ, 1, C) : slice_rsrc(p.w, base, ISZ, T, C);
-  const int in_row0 = (int)(t_lo + tau) * Ci * ISZ, in_step = LC * Ci * ISZ;
+  // byte offsets in unsigned 32-bit arithmetic, as in sweep()
+  const uint32_t in_row0 = (uint32_t)(t_lo + tau) * (uint32_t)Ci * ISZ, in_step = LC * (uint32_t)Ci * ISZ;
   Raw<BF16> buf[3];   // k, v, w rows of the lane's token
   auto fetch = [&](int ch) {
     const bool in_seg = tau < (int)min<int64_t>(LC, n - (int64_t)ch * LC);
-    const int row = in_row0 + ch * in_step;
-    const int off = in_seg ? row : kOffNone;
+    const int off = in_seg ? (int)(in_row0 + (uint32_t)ch * in_step) : kOffNone;
     buf[0] = gload<BF16>(rk, off, g);
     buf[1] = gload<BF16>(rv, off, g);
-    buf[2] = gload<BF16>(rw, in_seg ? (WS ? 0 : row) : kOffNone, g);
+    buf[2] = gload<BF16>(rw, WS ? (in_seg ? 0 : kOffNone) : off, g);
   };
   fetch(0);
 
