@@ -434,14 +434,17 @@ __device__ __forceinline__ float gate_at(const GateRaw<BF16>& g, int nt, int j) 
 // per-channel affine gamma, beta, times the gate, rounded to bf16 (nearest
 // even) and stored.  Lanes of a token past the segment store nothing
 // (their byte offset lies outside the slice).
+// Y is overwritten (its deviations from the row mean are formed in place, so
+// that no second set of 16 registers is live at this peak of the sweep).
 template <bool BF16>
-__device__ __forceinline__ void gn_gate_store(const f32x4 (&Y)[4], const GateRaw<BF16>& gt, const float* sGm,
+__device__ __forceinline__ void gn_gate_store(f32x4 (&Y)[4], const GateRaw<BF16>& gt, const float* sGm,
                                               const float* sBt, int g, float eps, Rsrc ro, int ooff) {
   float s = 0.f;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) s += (Y[nt][0] + Y[nt][1]) + (Y[nt][2] + Y[nt][3]);
   const float mean = rows_sum(s) * (1.f / 64.f);
-  float d[4][4], q = 0.f;
+  float q = 0.f;
+  f32x4 (&d)[4] = Y;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
