@@ -44,7 +44,7 @@ sys.path.insert(0, ROOT)
 
 from linear_attention_rnn_amd import inputs as I  # noqa: E402
 
-HEADLINE = "image-base-bidir-bf16"
+HEADLINE = "text-long-causal-bf16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak, published

@@ -27,27 +27,45 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the WKV-6 library needs ROCm's hipcc to build")
 
 
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libwkv6.so; returns its path.  Raises on failure."""
+    """Compile libwkv6.so; returns its path.  Raises on failure.  Each source
+    compiles to its own object in parallel, then one link step."""
     tmp = LIB + ".tmp"
-    cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Wall", "-Wno-unused-function",
         # packed fp32 VALU instructions stay off: plain scalar fp32 code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         f"-I{INCLUDE}", f"-I{CSRC}",
-        *[os.path.join(CSRC, s) for s in SOURCES],
-        "-o", tmp,
     ]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
-    if msgs.strip() and verbose:
-        print(msgs, flush=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        procs.append((src, _run([hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)))
+    failed = []
+    for src, pr in procs:
+        out, _ = pr.communicate()
+        msgs = "\n".join(l for l in out.splitlines() if noise not in l)
+        if pr.returncode != 0:
+            failed.append(f"{src} ({pr.returncode}):\n{msgs}")
+        elif msgs.strip() and verbose:
+            print(msgs, flush=True)
+    if failed:
+        raise RuntimeError("hipcc failed: " + "\n".join(failed))
+    link = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    out, _ = link.communicate()
+    if link.returncode != 0:
+        raise RuntimeError(f"link failed ({link.returncode}):\n{out}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -39,8 +39,14 @@ int check_sizes(int64_t B, int64_t T, int64_t C, int64_t H, int mode, int dtype)
     return fail(WKV6_ERR_INVALID_ARG, "unknown dtype");
   if (C / H != wkv6::kHead) return fail(WKV6_ERR_UNSUPPORTED, "head size C/H must be 64");
   if (B == 0 || T == 0) return WKV6_OK;
+  // One workgroup of 256 work-items per (batch, head) pair: the launch's
+  // B * H * 256 work-items must stay below 2^32.  (Segmented launches only
+  // happen when B * H is below a few hundred.)  Checked by division, so that
+  // no product overflows.
+  if (H > wkv6::kMaxItems || B > wkv6::kMaxItems / H)
+    return fail(WKV6_ERR_UNSUPPORTED, "B * H exceeds the supported number of (batch, head) pairs (2^24 - 1)");
   // the kernels address one (batch, head) slice with 32-bit byte offsets
-  if (T > INT_MAX - wkv6::kChunk || B * H > INT_MAX || B > INT64_MAX / T || B * T > INT64_MAX / (4 * C) ||
+  if (T > INT_MAX - wkv6::kChunk || B > INT64_MAX / T || B * T > INT64_MAX / (4 * C) ||
       T > (INT_MAX - 4096) / (4 * C))
     return fail(WKV6_ERR_UNSUPPORTED, "sizes exceed the supported index range");
   return WKV6_OK;

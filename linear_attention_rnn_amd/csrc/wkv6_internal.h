@@ -10,6 +10,9 @@ namespace wkv6 {
 // Head size and chunk length the kernels are built for.
 constexpr int kHead = 64;
 constexpr int kChunk = 64;
+// Most (batch, head) pairs one call accepts: one 256-work-item workgroup
+// each, and a launch holds fewer than 2^32 work-items.
+constexpr int64_t kMaxItems = (int64_t(1) << 24) - 1;
 
 struct FwdArgs {
   int64_t B, T, C, H;

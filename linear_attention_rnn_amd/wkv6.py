@@ -144,7 +144,18 @@ def _check_inputs(r, k, v, w_raw, u, w_static=False):
     for name, t in (("r", r), ("k", k), ("v", v), ("w_raw", w_raw), ("u", u)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if t.device != r.device:
+            raise ValueError(f"{name} must be on the same GPU as r")
     return B, T, C, dtype
+
+
+def _check_out(t, shape, dtype, device, name: str):
+    """A caller-supplied output buffer: a contiguous tensor of the given shape
+    and dtype on the inputs' GPU.  A host tensor would hand the kernels a host
+    address to store through, so it is refused here, before any library call."""
+    if (not getattr(t, "is_cuda", False) or t.device != device or tuple(t.shape) != tuple(shape)
+            or t.dtype != dtype or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {list(shape)} on {device}")
 
 
 def _stream_handle(stream, device):
@@ -171,15 +182,16 @@ def fwd_state(r, k, v, w_raw, u, H: int, s_in=None, want_state: bool = True, out
     if s_in is not None and (s_in.shape != shape or s_in.dtype != torch.float32 or not s_in.is_cuda
                              or not s_in.is_contiguous()):
         raise ValueError("s_in must be a contiguous float32 GPU tensor [B, H, 64, 64]")
+    if s_in is not None and s_in.device != r.device:
+        raise ValueError("s_in must be on the inputs' GPU")
     if out is None:
         out = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
-    elif out.shape != (B, T, C) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
+    else:
+        _check_out(out, (B, T, C), torch.float32, r.device, "out")
     if s_out is None and want_state:
         s_out = torch.empty(shape, dtype=torch.float32, device=r.device)
-    elif s_out is not None and (s_out.shape != shape or s_out.dtype != torch.float32
-                                or not s_out.is_contiguous()):
-        raise ValueError("s_out must be a contiguous float32 [B, H, 64, 64] tensor")
+    elif s_out is not None:
+        _check_out(s_out, shape, torch.float32, r.device, "s_out")
     st = fwd_state_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
                        u.data_ptr(), out.data_ptr(), 0 if s_in is None else s_in.data_ptr(),
                        0 if s_out is None else s_out.data_ptr(), dtype,
@@ -203,8 +215,8 @@ def fwd(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
     B, T, C, dtype = _check_inputs(r, k, v, w_raw, u)
     if out is None:
         out = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
-    elif out.shape != (B, T, C) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
+    else:
+        _check_out(out, (B, T, C), torch.float32, r.device, "out")
     st = fwd_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
                  u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, _stream_handle(stream, r.device))
     if st != OK:
@@ -225,8 +237,8 @@ def fwd5(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None)
     B, T, C, dtype = _check_inputs(r, k, v, w_raw, u, w_static=True)
     if out is None:
         out = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
-    elif out.shape != (B, T, C) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
+    else:
+        _check_out(out, (B, T, C), torch.float32, r.device, "out")
     st = fwd5_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
                   u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, _stream_handle(stream, r.device))
     if st != OK:
@@ -251,8 +263,8 @@ def fwd_gn(r, k, v, w_raw, u, g, gamma, beta, H: int, mode: str = "causal", eps:
             raise ValueError(f"{name} must be a contiguous float32 GPU tensor of C values")
     if out is None:
         out = torch.empty((B, T, C), dtype=torch.bfloat16, device=r.device)
-    elif out.shape != (B, T, C) or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 [B, T, C] tensor")
+    else:
+        _check_out(out, (B, T, C), torch.bfloat16, r.device, "out")
     st = fwd_gn_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(), u.data_ptr(),
                     g.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps), out.data_ptr(), _MODES[mode],
                     dtype, _stream_handle(stream, r.device))
@@ -283,8 +295,8 @@ def fwd4(k, v, w, u, out=None, stream=None):
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     if out is None:
         out = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
-    elif out.shape != (B, T, C) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B, T, C] tensor")
+    else:
+        _check_out(out, (B, T, C), torch.float32, k.device, "out")
     st = fwd4_raw(B, T, C, k.data_ptr(), v.data_ptr(), w.data_ptr(), u.data_ptr(), out.data_ptr(), dtype,
                   _stream_handle(stream, k.device))
     if st != OK:

@@ -51,6 +51,9 @@ def _call(B=2, T=8, C=128, H=2, ptrs=None, mode=0, dtype=0):
     (dict(C=256, H=2), wkv6.ERR_UNSUPPORTED),     # head size 128
     (dict(T=2 ** 31), wkv6.ERR_UNSUPPORTED),
     (dict(T=2 ** 20, C=512, H=8), wkv6.ERR_UNSUPPORTED),   # one slice beyond 2 GiB of fp32 rows
+    (dict(B=2 ** 24, T=1, C=64, H=1), wkv6.ERR_UNSUPPORTED),   # B * H * 256 work-items reach 2^32
+    (dict(B=2 ** 12, T=1, C=64 * 2 ** 12, H=2 ** 12), wkv6.ERR_UNSUPPORTED),
+    (dict(B=2 ** 62, T=1, C=64 * 2 ** 10, H=2 ** 10), wkv6.ERR_UNSUPPORTED),   # B * H overflows int64
 ])
 def test_rejects_bad_arguments(kw, status):
     assert _call(**kw) == status

@@ -81,6 +81,17 @@ def test_backward_long_sequence(torch_cuda):
     check("long causal", x, dy_of(x, 84), H, "causal", "f32")
 
 
+def test_backward_image_hires_full(torch_cuda):
+    """The benched image-hires shape (B = 4, T = 4096, C = 1024, H = 16,
+    bidirectional, bf16, 10% of channels at w_raw = -9) with the planner's
+    own segment count (the sequences are cut into segments there), every
+    gradient compared with the oracle over the whole tensor."""
+    w = I.workload("image-hires-bidir-bf16")
+    x = I.make_inputs(w)
+    say(f"[backward] image-hires full: B={w.B} T={w.T} C={w.C} H={w.H}")
+    check("image-hires full (default segments)", x, dy_of(x, w.seed + 1000), w.H, w.mode, w.dtype)
+
+
 @pytest.mark.parametrize("case", ["no_decay", "fast_decay", "mixed"])
 def test_backward_decay_extremes(torch_cuda, case):
     B, T, H = 2, 40, 2

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from linear_attention_rnn_amd import inputs as I
-from oracle import group_norm_heads, wkv6_ref
+from oracle import wkv6_gn_ref, wkv6_ref
 from tests.gpu_util import device_inputs, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -55,13 +55,15 @@ def run_gn(x, g, gamma, beta, H, mode, dtype, eps=EPS):
 
 
 def check(tag, x, g, gamma, beta, H, mode, dtype, out, eps=EPS):
+    """out against wkv6_gn_ref; the per-element bound needs the operator's y
+    and the normalised z of each head row, taken from the oracle as well."""
+    ref = wkv6_gn_ref(x["r"], x["k"], x["v"], x["w_raw"], x["u"], g, gamma, beta, eps, H, mode)
     y = wkv6_ref(x["r"], x["k"], x["v"], x["w_raw"], x["u"], H, mode)
     B, T, C = y.shape
     yh = y.reshape(B, T, H, 64)
     s = np.sqrt(yh.var(-1) + eps)[..., None]
     z = ((yh - yh.mean(-1, keepdims=True)) / s).reshape(B, T, C)
     s = np.broadcast_to(s, yh.shape).reshape(B, T, C)
-    ref = group_norm_heads(y, H, gamma, beta, eps) * g
     gg = np.abs(gamma * g)
     bound = (2.0 ** -8 * np.abs(ref) + (2.0 + np.abs(z)) * TOL_Y[dtype] * np.sqrt(np.mean(y ** 2)) / s * gg
              + 1e-6 * (gg + np.abs(beta * g)))
@@ -118,16 +120,14 @@ def test_gn_repeated_calls_reuse_clean_markers(torch_cuda):
           run_gn(x2, g, gamma, beta, H, "bidirectional", "f32"))
 
 
-def test_gn_image_base_shape_sampled(torch_cuda):
+def test_gn_image_base_shape_full(torch_cuda):
     """Full image-base size (B = 64, T = 196, C = 768, H = 12, bidirectional,
-    bf16) in one call; three batch items checked against the oracle."""
+    bf16) in one call; every batch item checked against the oracle."""
     B, T, C, H = 64, 196, 768, 12
     x = I.random_inputs(B, T, C, H, seed=740, dtype="bf16")
     g, gamma, beta = extras(B, T, C, 741, "bf16")
     out = run_gn(x, g, gamma, beta, H, "bidirectional", "bf16")
-    for b in (0, 31, 63):
-        xs = {key: (val[b:b + 1] if val.ndim == 3 else val) for key, val in x.items()}
-        check(f"image-base item {b}", xs, g[b:b + 1], gamma, beta, H, "bidirectional", "bf16", out[b:b + 1])
+    check("image-base, all 64 items", x, g, gamma, beta, H, "bidirectional", "bf16", out)
 
 
 def test_gn_zero_eps_and_constant_rows(torch_cuda):

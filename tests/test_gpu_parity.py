@@ -9,14 +9,14 @@ import pytest
 
 from linear_attention_rnn_amd import inputs as I
 from oracle import wkv6_ref
-from tests.gpu_util import err_over_rms, gpu_fwd, head_slice, say, device_inputs
+from tests.gpu_util import err_over_rms, gpu_fwd, say, device_inputs
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 5e-3}
 
-SMALL = ["tiny-causal-f32", "image-tiny-bidir-f32", "image-base-bidir-bf16"]
-LARGE = ["text-long-causal-bf16", "image-hires-bidir-bf16"]
+WORKLOADS = ["tiny-causal-f32", "image-tiny-bidir-f32", "image-base-bidir-bf16", "text-long-causal-bf16",
+             "image-hires-bidir-bf16"]
 
 
 @pytest.fixture(scope="module")
@@ -27,38 +27,24 @@ def torch_cuda():
     return torch
 
 
-@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("name", WORKLOADS)
 def test_workload_full_parity(torch_cuda, name):
+    """Every output of the full-size launch against the oracle over every
+    (batch, head) pair: the global max|y - y_ref| over all B*T*C outputs
+    divided by the global rms of y_ref.  Per-head maxima are printed for
+    diagnosis."""
     w = I.workload(name)
     x = I.make_inputs(w)
     say(f"[parity] {name}: B={w.B} T={w.T} C={w.C} H={w.H} {w.mode} {w.dtype}")
     y = gpu_fwd(x, w.H, w.mode, w.dtype)
+    say(f"[parity] {name}: GPU done, running the oracle")
     y_ref = wkv6_ref(x["r"], x["k"], x["v"], x["w_raw"], x["u"], w.H, w.mode)
     e = err_over_rms(y, y_ref)
-    say(f"[parity] {name}: max|dy|/rms = {e:.3e} (tol {w.tolerance:g})")
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    per_head = np.abs(y - y_ref).reshape(w.B, w.T, w.H, 64).max(axis=(0, 1, 3)) / rms
+    say(f"[parity] {name}: max|dy|/rms = {e:.3e} (tol {w.tolerance:g}); worst head {int(per_head.argmax())} "
+        f"{per_head.max():.3e}, best head {per_head.min():.3e}")
     assert e <= w.tolerance
-
-
-@pytest.mark.parametrize("name", LARGE)
-def test_workload_sampled_parity(torch_cuda, name):
-    """Full-size launch; the oracle evaluates sampled (batch, head) pairs."""
-    w = I.workload(name)
-    x = I.make_inputs(w)
-    say(f"[parity] {name}: B={w.B} T={w.T} C={w.C} H={w.H} {w.mode} {w.dtype} (sampled)")
-    y = gpu_fwd(x, w.H, w.mode, w.dtype)
-    assert np.all(np.isfinite(y))
-    rng = np.random.default_rng(123)
-    pairs = {(0, 0), (w.B - 1, w.H - 1)}
-    while len(pairs) < 6:
-        pairs.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
-    worst = 0.0
-    for b, h in sorted(pairs):
-        xs = head_slice(x, b, h)
-        y_ref = wkv6_ref(xs["r"], xs["k"], xs["v"], xs["w_raw"], xs["u"], 1, w.mode)
-        e = err_over_rms(y[b:b + 1, :, h * 64:(h + 1) * 64], y_ref)
-        worst = max(worst, e)
-        say(f"[parity] {name}: (b={b}, h={h}) max|dy|/rms = {e:.3e}")
-    assert worst <= w.tolerance
 
 
 SHAPES_T = [1, 2, 3, 15, 16, 17, 31, 63, 64, 65, 127, 128, 129, 196, 257]

@@ -48,6 +48,48 @@ def test_scale_and_shift_of_a_head_do_not_matter():
     np.testing.assert_allclose((z ** 2).mean(-1), 1.0, rtol=1e-12)
 
 
+def test_fused_reference_hand_worked_single_token():
+    """wkv6_gn_ref through the operator, worked by hand.  With one token the
+    operator's output is the u-weighted current token alone, y_0 = (sum_c
+    r_0[c] u[c] k_0[c]) v_0, in both modes (no earlier and no later token).
+    Here r_0 = (1, 2, 0, 0), u = (0.5, 0.25, 3, 3), k_0 = (1, 1, 0, 0) give
+    the weight 1/2 + 1/2 = 1, so y_0 = v_0 = (1, 2, 3, 6), and the worked
+    normalisation above (eps = 1/2, gamma = 1, 2, 1, 1, beta = 0, 0, 1, 0,
+    gate 2, 1, 1, -1) gives -2, -1, 1, -3/2.  A second head has r scaled by 10
+    and u by 1/10, so its weight and its row are the same."""
+    r = np.array([[[1.0, 2.0, 0.0, 0.0, 10.0, 20.0, 0.0, 0.0]]])
+    k = np.array([[[1.0, 1.0, 0.0, 0.0, 1.0, 1.0, 0.0, 0.0]]])
+    u = np.array([0.5, 0.25, 3.0, 3.0, 0.05, 0.025, 7.0, 7.0])
+    v = np.array([[[1.0, 2.0, 3.0, 6.0, 1.0, 2.0, 3.0, 6.0]]])
+    w_raw = np.array([[[0.3, -1.0, 2.0, -5.0, 0.0, 0.0, 1.0, 1.0]]])   # a single token never decays
+    gamma = np.array([1.0, 2.0, 1.0, 1.0] * 2)
+    beta = np.array([0.0, 0.0, 1.0, 0.0] * 2)
+    g = np.array([[[2.0, 1.0, 1.0, -1.0] * 2]])
+    for mode in ("causal", "bidirectional"):
+        out = wkv6_gn_ref(r, k, v, w_raw, u, g, gamma, beta, 0.5, 2, mode)
+        np.testing.assert_allclose(out[0, 0], [-2.0, -1.0, 1.0, -1.5] * 2, rtol=1e-12)
+
+
+def test_fused_reference_hand_worked_two_tokens():
+    """Two tokens, one head of N = 2, causal: y_0 = (r_0 . u k_0) v_0 and
+    y_1 = r_1 . (k_0^T v_0 + diag(u) k_1^T v_1) (the first token reaches the
+    second with weight 1: no decay lies strictly between them).  With
+    r_0 = (1, 0), k_0 = (1, 0), v_0 = (1, 3), r_1 = (1, 1), k_1 = (0, 2),
+    v_1 = (2, 2), u = (1, 1): y_0 = (1, 3) and y_1 = (1 + 4, 3 + 4) = (5, 7).
+    Each row has mean m and half-spread d, so with eps = 0 it normalises to
+    (-1, +1); gamma = (2, 1), beta = (1, 0), gate (1, -1) give (-1, -1).
+    Bidirectional adds r_0 . k_1^T v_1 = 0 to y_0 and nothing to y_1."""
+    r = np.array([[[1.0, 0.0], [1.0, 1.0]]])
+    k = np.array([[[1.0, 0.0], [0.0, 2.0]]])
+    v = np.array([[[1.0, 3.0], [2.0, 2.0]]])
+    w_raw = np.array([[[0.7, -0.2], [1.1, 0.4]]])
+    u = np.array([1.0, 1.0])
+    g = np.array([[[1.0, -1.0], [1.0, -1.0]]])
+    for mode in ("causal", "bidirectional"):
+        out = wkv6_gn_ref(r, k, v, w_raw, u, g, [2.0, 1.0], [1.0, 0.0], 0.0, 1, mode)
+        np.testing.assert_allclose(out[0], [[-1.0, -1.0], [-1.0, -1.0]], rtol=1e-12, atol=1e-12)
+
+
 def test_fused_reference_is_the_composition():
     rng = np.random.default_rng(8)
     B, T, H = 1, 7, 2
