@@ -183,17 +183,25 @@ __device__ __forceinline__ float at(float4 x, int i) { return i == 0 ? x.x : i =
 constexpr int TB = 16;
 
 struct Smem {
-  float r[TB][HS], k[TB][HS], w[TB][HS], x[TB][HS], lam[TB][HS], v[TB][HS], dy[TB][HS];
+  float r[TB][HS], k[TB][HS], dlt[TB][HS], x[TB][HS], lam[TB][HS], v[TB][HS], dy[TB][HS];   // dlt = 1 - w
   float dyv[TB];
   float oa[TB][HS], ob[TB][HS];        // per token: dr (pass 1); dk and D (pass 2)
   float ov[TB][NT / 64][HS];          // per token and wave: partial column sums for dv
 };
 
-// Decay of a staged value: lambda = -exp(w_raw), w = exp(lambda).
-__device__ __forceinline__ void decay4(float4 wr, float4& lam, float4& w) {
+// Decay of a staged value: lambda = -exp(w_raw) and dlt = 1 - w =
+// -expm1(lambda).  The recurrences decay by x <- x - dlt x, never by a product
+// with w itself: for slow decays w lies within 1e-4 of 1, where float32
+// keeps only a few significant digits of 1 - w, and that relative error of
+// the decay compounds over thousands of tokens (1e-4 of the state after 4096
+// tokens at w_raw = -9), while dlt keeps full float32 precision.
+__device__ __forceinline__ void decay4(float4 wr, float4& lam, float4& dlt) {
   lam = make_float4(-ex2(wr.x * kLog2e), -ex2(wr.y * kLog2e), -ex2(wr.z * kLog2e), -ex2(wr.w * kLog2e));
-  w = make_float4(ex2(lam.x * kLog2e), ex2(lam.y * kLog2e), ex2(lam.z * kLog2e), ex2(lam.w * kLog2e));
+  dlt = make_float4(-expm1f(lam.x), -expm1f(lam.y), -expm1f(lam.z), -expm1f(lam.w));
 }
+
+// x <- w x + a with w = 1 - dlt.
+__device__ __forceinline__ float decay_add(float dlt, float x, float a) { return fmaf(-dlt, x, x + a); }
 
 // One thread's share of a block as loaded from HBM (zeros past the end).
 template <bool BF16>
@@ -293,10 +301,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       {
         const bool ok = pos(bi) < q1;
         const float4 k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v));
-        float4 lam, w;
-        decay4(widen(x.w), lam, w);
+        float4 lam, dlt;
+        decay4(widen(x.w), lam, dlt);
         st4(&sm.k[ts][cc], k);
-        st4(&sm.w[ts][cc], w);
+        st4(&sm.dlt[ts][cc], dlt);
         st4(&sm.v[ts][cc], v);
         const float4 dy = keep(ok, x.dy);
         st4(&sm.dy[ts][cc], dy);
@@ -306,12 +314,12 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       if (REV) old_dr = f4(p.dr + at_q(bi));
       load(bi + 1 < nblk ? bi + 1 : bi);
       struct Tk {
-        float4 k, w, v, dy;
+        float4 k, dl, v, dy;   // dl = 1 - w
       };
       auto rd = [&](int tt) {
         Tk e;
         e.k = f4(&sm.k[tt][c0]);
-        e.w = f4(&sm.w[tt][c0]);
+        e.dl = f4(&sm.dlt[tt][c0]);
         e.v = f4(&sm.v[tt][n0]);
         e.dy = f4(&sm.dy[tt][n0]);
         return e;
@@ -330,11 +338,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float ki = at(e.k, i), wi = at(e.w, i);
-          S[i][0] = fmaf(wi, S[i][0], ki * e.v.x);
-          S[i][1] = fmaf(wi, S[i][1], ki * e.v.y);
-          S[i][2] = fmaf(wi, S[i][2], ki * e.v.z);
-          S[i][3] = fmaf(wi, S[i][3], ki * e.v.w);
+          const float ki = at(e.k, i), di = at(e.dl, i);
+          S[i][0] = decay_add(di, S[i][0], ki * e.v.x);
+          S[i][1] = decay_add(di, S[i][1], ki * e.v.y);
+          S[i][2] = decay_add(di, S[i][2], ki * e.v.z);
+          S[i][3] = decay_add(di, S[i][3], ki * e.v.w);
         }
       }
     }
@@ -418,10 +426,10 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       {
         const bool ok = pos(bi) < q1;
         const float4 r = keep(ok, widen(x.r)), dy = keep(ok, x.dy);
-        float4 lam, w;
-        decay4(widen(x.w), lam, w);
+        float4 lam, dlt;
+        decay4(widen(x.w), lam, dlt);
         st4(&sm.r[ts][cc], r);
-        st4(&sm.w[ts][cc], w);
+        st4(&sm.dlt[ts][cc], dlt);
         st4(&sm.dy[ts][cc], dy);
         const float4 k = keep(ok, widen(x.k)), v = keep(ok, widen(x.v)), dr = keep(ok, x.dr);
         st4(&sm.k[ts][cc], k);
@@ -434,13 +442,13 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
       if (REV) load_old(bi);
       load(bi > 0 ? bi - 1 : 0);
       struct Tk {
-        float4 r, k, w, v, dy;
+        float4 r, k, dl, v, dy;   // dl = 1 - w
         float d, ki, rdri, rui;   // dy . v; k, r dr and r u of row c0 + ri
       };
       auto rd = [&](int tt) {
         Tk e;
         e.r = f4(&sm.r[tt][c0]);
-        e.w = f4(&sm.w[tt][c0]);
+        e.dl = f4(&sm.dlt[tt][c0]);
         e.dy = f4(&sm.dy[tt][n0]);
         e.k = f4(&sm.k[tt][c0]);
         e.v = f4(&sm.v[tt][n0]);
@@ -477,11 +485,11 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float ri_ = at(e.r, i), wi = at(e.w, i);
-          G[i][0] = fmaf(wi, G[i][0], ri_ * e.dy.x);
-          G[i][1] = fmaf(wi, G[i][1], ri_ * e.dy.y);
-          G[i][2] = fmaf(wi, G[i][2], ri_ * e.dy.z);
-          G[i][3] = fmaf(wi, G[i][3], ri_ * e.dy.w);
+          const float ri_ = at(e.r, i), di = at(e.dl, i);
+          G[i][0] = decay_add(di, G[i][0], ri_ * e.dy.x);
+          G[i][1] = decay_add(di, G[i][1], ri_ * e.dy.y);
+          G[i][2] = decay_add(di, G[i][2], ri_ * e.dy.z);
+          G[i][3] = decay_add(di, G[i][3], ri_ * e.dy.w);
         }
       }
     }
@@ -507,6 +515,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 // A segment's summaries for the carry kernel, in one pass over its sweep
 // positions in order (one workgroup per batch item, head and segment):
 //   Sl  its state after its last token, from zero: S <- w S + k^T v;
+//       (every decay here is applied as x - (1 - w) x; see decay4)
 //   Gl  its adjoint before its first token, from zero after its last:
 //       sum_q (prod of w over the segment's positions before q) r_q^T dy_q.
 //       No term of that sum depends on another, so it accumulates in the
@@ -516,7 +525,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
 // The state of the last segment and the adjoint of the first are never read
 // and not stored.
 struct SummSmem {
-  float r[TB][HS], k[TB][HS], w[TB][HS], v[TB][HS], dy[TB][HS];
+  float r[TB][HS], k[TB][HS], dlt[TB][HS], v[TB][HS], dy[TB][HS];   // dlt = 1 - w
   float red[NT / 64][HS];
 };
 
@@ -567,11 +576,11 @@ __global__ __launch_bounds__(NT) void bwd_summary_kernel(BwdParams p) {
       // past the end: zero keys, values, queries and output gradients (their
       // decays only touch summaries after the last real position)
       const bool ok = pos(bi) < q1;
-      float4 lam, w;
-      decay4(widen(x.w), lam, w);
+      float4 lam, dlt;
+      decay4(widen(x.w), lam, dlt);
       st4(&sm.r[ts][cc], keep(ok, widen(x.r)));
       st4(&sm.k[ts][cc], keep(ok, widen(x.k)));
-      st4(&sm.w[ts][cc], w);
+      st4(&sm.dlt[ts][cc], dlt);
       st4(&sm.v[ts][cc], keep(ok, widen(x.v)));
       st4(&sm.dy[ts][cc], keep(ok, x.dy));
       if (ok) {
@@ -584,13 +593,13 @@ __global__ __launch_bounds__(NT) void bwd_summary_kernel(BwdParams p) {
     __syncthreads();
     load(bi + 1 < nblk ? bi + 1 : bi);
     struct Tk {
-      float4 r, k, w, v, dy;
+      float4 r, k, dl, v, dy;   // dl = 1 - w
     };
     auto rd = [&](int tt) {
       Tk e;
       e.r = f4(&sm.r[tt][c0]);
       e.k = f4(&sm.k[tt][c0]);
-      e.w = f4(&sm.w[tt][c0]);
+      e.dl = f4(&sm.dlt[tt][c0]);
       e.v = f4(&sm.v[tt][n0]);
       e.dy = f4(&sm.dy[tt][n0]);
       return e;
@@ -602,16 +611,16 @@ __global__ __launch_bounds__(NT) void bwd_summary_kernel(BwdParams p) {
       if (tt + 1 < TB) nx = rd(tt + 1);   // the next token's operands are in flight during this one
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ki = at(e.k, i), wi = at(e.w, i), pr = P[i] * at(e.r, i);
-        S[i][0] = fmaf(wi, S[i][0], ki * e.v.x);
-        S[i][1] = fmaf(wi, S[i][1], ki * e.v.y);
-        S[i][2] = fmaf(wi, S[i][2], ki * e.v.z);
-        S[i][3] = fmaf(wi, S[i][3], ki * e.v.w);
+        const float ki = at(e.k, i), di = at(e.dl, i), pr = P[i] * at(e.r, i);
+        S[i][0] = decay_add(di, S[i][0], ki * e.v.x);
+        S[i][1] = decay_add(di, S[i][1], ki * e.v.y);
+        S[i][2] = decay_add(di, S[i][2], ki * e.v.z);
+        S[i][3] = decay_add(di, S[i][3], ki * e.v.w);
         G[i][0] = fmaf(pr, e.dy.x, G[i][0]);
         G[i][1] = fmaf(pr, e.dy.y, G[i][1]);
         G[i][2] = fmaf(pr, e.dy.z, G[i][2]);
         G[i][3] = fmaf(pr, e.dy.w, G[i][3]);
-        P[i] *= wi;
+        P[i] = fmaf(-di, P[i], P[i]);
       }
     }
   }

@@ -1518,7 +1518,8 @@ __global__ __launch_bounds__(NT) void state_copy_kernel(const float* __restrict_
 // 4 (t % 16) .. + 3.  Per token: y_t[n] = sum_c r_t[c] S[c][n] + d_t v_t[n]
 // with d_t = sum_c r_t[c] u[c] k_t[c] (partial sums over the thread's rows,
 // combined across the 16 row groups through LDS), then
-// S[c][n] <- w_t[c] S[c][n] + k_t[c] v_t[n].  fp32 throughout.
+// S[c][n] <- w_t[c] S[c][n] + k_t[c] v_t[n] (as S + kv - (1 - w) S).  fp32
+// throughout.
 constexpr int kDecodeMaxT = 4;
 
 template <bool BF16>
@@ -1556,12 +1557,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(Params p) {
   const float ul = p.u[h * HS + lane];
   for (int tok = 0; tok < p.T; ++tok) {
     const int64_t row = ((int64_t)b * p.T + tok) * p.C + (int64_t)h * HS;
-    float r[4], k[4], w[4], v[4];
+    // dl = 1 - w = -expm1(-exp(w_raw)): the state decays as S - dl S, so a
+    // decay within 1e-4 of 1 keeps its full precision over many calls (a
+    // product with w rounded to float32 would bias a long-memory state)
+    float r[4], k[4], dl[4], v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       r[i] = load_elem<BF16>(p.r, row + c0 + i);
       k[i] = load_elem<BF16>(p.k, row + c0 + i);
-      w[i] = ex2(-kLog2e * ex2(load_elem<BF16>(p.w, (p.w_static ? (int64_t)h * HS : row) + c0 + i) * kLog2e));
+      dl[i] = -expm1f(-ex2(load_elem<BF16>(p.w, (p.w_static ? (int64_t)h * HS : row) + c0 + i) * kLog2e));
       v[i] = load_elem<BF16>(p.v, row + n0 + i);
     }
     // partial y over the thread's four rows, summed over the row groups of
@@ -1598,7 +1602,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[i][j] = fmaf(w[i], S[i][j], k[i] * v[j]);
+      for (int j = 0; j < 4; ++j) S[i][j] = fmaf(-dl[i], S[i][j], fmaf(k[i], v[j], S[i][j]));
   }
   if (p.s_out) {
     float* so = p.s_out + (int64_t)bh * PL;

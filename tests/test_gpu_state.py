@@ -141,6 +141,32 @@ def test_token_by_token_decode(torch_cuda, dtype):
     check(f"decode {dtype}", np.concatenate(ys, axis=1), S, y_ref, S_ref, dtype)
 
 
+def test_long_streaming_decode_keeps_slow_decays(torch_cuda):
+    """2048 one-token calls with the state kept on the GPU between them, at
+    decays within 1.2e-4 of 1 (w_raw = -9) and a few faster ones: the state
+    and outputs stay within the float32 bound of the oracle over the whole
+    stream (a decay applied as a product with w rounded to float32 would
+    drift by about 1e-4 of the state here)."""
+    import torch
+    from linear_attention_rnn_amd import wkv6
+
+    B, H, T = 2, 2, 2048
+    x = I.random_inputs(B, T, 64 * H, H, seed=49, dtype="f32", wraw_lo=-9.0, wraw_hi=-9.0)
+    x["w_raw"][..., ::7] = -2.0
+    S0 = state_of(B, H, 50, scale=0.3)
+    d = device_inputs(x, "f32")
+    S = torch.from_numpy(S0).cuda()
+    S_next = torch.empty_like(S)
+    y = torch.empty((B, T, 64 * H), device="cuda")
+    for t in range(T):
+        yt, _ = wkv6.fwd_state(*(a[:, t:t + 1].contiguous() for a in d[:4]), d[4], H, s_in=S, s_out=S_next)
+        y[:, t:t + 1] = yt
+        S, S_next = S_next, S
+    torch.cuda.synchronize()
+    y_ref, S_ref = ref_state(x, H, S0)
+    check("streaming decode 2048 tokens", y.double().cpu().numpy(), S.double().cpu().numpy(), y_ref, S_ref, "f32")
+
+
 def test_empty_sequence_passes_the_state(torch_cuda):
     torch = torch_cuda
     from linear_attention_rnn_amd import wkv6
