@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define WKV6_ABI_VERSION 4
+#define WKV6_ABI_VERSION 5
 
 /* mode */
 #define WKV6_MODE_CAUSAL        0
@@ -103,6 +103,32 @@ extern "C" {
 int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H,
              const void* r, const void* k, const void* v, const void* w_raw,
              const float* u, float* y, int mode, int dtype, void* stream);
+
+/*
+ * wkv6_fwd_noalloc -- wkv6_fwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It calls no hipMalloc, hipFree or allocating library
+ * routine.
+ *
+ * Arguments, layout, results, execution and errors as wkv6_fwd.  The segment
+ * summaries of a segmented call live in a static device array of the
+ * library, 32 MiB per GPU, held from the first use until the process ends
+ * (its address is taken once per device, on the first call on that device).
+ * A call whose planned segment count would need more than that runs with
+ * fewer segments (the result differs from wkv6_fwd's by rounding only);
+ * since an unsegmented call needs no scratch, every size wkv6_fwd accepts is
+ * accepted here.  UNSUPPORTED reports a workspace beyond the array should a
+ * future variant need one.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * there: calls that can overlap on one GPU (on different streams, or from
+ * different host threads without ordering) race on it and must not be made.
+ * Calls ordered on one stream are safe; nothing in the array needs to start
+ * at zero.
+ */
+int wkv6_fwd_noalloc(int64_t B, int64_t T, int64_t C, int64_t H,
+                     const void* r, const void* k, const void* v, const void* w_raw,
+                     const float* u, float* y, int mode, int dtype, void* stream);
 
 /*
  * wkv6_fwd_gn -- wkv6_fwd followed by the block's output normalisation and

@@ -179,6 +179,21 @@ int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const vo
   return run(make_args(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype), static_cast<hipStream_t>(stream));
 }
 
+int wkv6_fwd_noalloc(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k,
+                     const void* v, const void* w_raw, const float* u, float* y, int mode, int dtype,
+                     void* stream) {
+  g_last_error.clear();
+  int st = check_sizes(B, T, C, H, mode, dtype);
+  if (st != WKV6_OK || B == 0 || T == 0) return st;
+  if ((st = check_tensors(B, T, C, dtype, r, k, v, w_raw, u, y)) != WKV6_OK) return st;
+  const hipError_t e = wkv6::enqueue_fwd_noalloc(make_args(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype),
+                                                 static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue)
+    return fail(WKV6_ERR_UNSUPPORTED, "the call's workspace exceeds the library's 32 MiB scratch array");
+  if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return WKV6_OK;
+}
+
 int wkv5_fwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k,
              const void* v, const void* w_raw, const float* u, float* y, int mode, int dtype,
              void* stream) {

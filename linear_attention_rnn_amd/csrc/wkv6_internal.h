@@ -45,6 +45,15 @@ size_t workspace_bytes(const FwdArgs& a);
 // Returns the first HIP error, if any.
 hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream);
 
+// Size of the library's static per-device scratch array (wkv6_fwd_noalloc).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+
+// The plain forward (no state, no epilogue) with its workspace in the
+// static scratch array instead of an allocation: the segment count is
+// lowered until the segment summaries fit in kScratchBytes.  Fails with
+// hipErrorInvalidValue if even an unsegmented call would need more.
+hipError_t enqueue_fwd_noalloc(const FwdArgs& a, hipStream_t stream);
+
 struct BwdArgs {
   int64_t B, T, C, H;
   const void* r;

@@ -77,6 +77,8 @@
 #include <stdint.h>
 
 #include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "wkv6_internal.h"
 
@@ -1714,11 +1716,55 @@ hipError_t launch_ws(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) 
                          : launch_t<BF16, false, WS, EPI>(a, pl, ws, s);
 }
 
+// Workspace of wkv6_fwd_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept per device.
+__device__ __align__(256) char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 size_t workspace_bytes(const FwdArgs& a) {
   if (a.B == 0 || a.T == 0 || (!a.bidirectional && !a.epi && a.T <= kDecodeMaxT)) return 0;
   return ws_layout(a, plan(a)).total;
+}
+
+hipError_t enqueue_fwd_noalloc(const FwdArgs& a, hipStream_t stream) {
+  if (a.epi || a.s_in || a.s_out || a.w_static) return hipErrorInvalidValue;   // plain forward only
+  if (a.T == 0 || a.B == 0) return hipSuccess;
+  if (!a.bidirectional && a.T <= kDecodeMaxT) return enqueue_fwd(a, nullptr, stream);   // no workspace
+  // the planner's segment count, lowered until the summaries fit the scratch
+  Plan pl = plan(a);
+  while (ws_layout(a, pl).total > kScratchBytes && pl.G > 1) {
+    const int G = pl.G - 1;
+    pl.SEGC = (pl.NC + G - 1) / G;
+    pl.G = (pl.NC + pl.SEGC - 1) / pl.SEGC;
+  }
+  if (ws_layout(a, pl).total > kScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  if (a.bf16) return launch_ws<true, false, false>(a, pl, ws, stream);
+  return launch_ws<false, false, false>(a, pl, ws, stream);
 }
 
 hipError_t enqueue_fwd(const FwdArgs& a, void* workspace, hipStream_t stream) {

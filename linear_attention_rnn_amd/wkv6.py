@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.wkv6_fwd.restype = ctypes.c_int
         L.wkv5_fwd.argtypes = L.wkv6_fwd.argtypes
         L.wkv5_fwd.restype = ctypes.c_int
+        L.wkv6_fwd_noalloc.argtypes = L.wkv6_fwd.argtypes
+        L.wkv6_fwd_noalloc.restype = ctypes.c_int
         L.wkv6_fwd_gn.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                   ctypes.c_int, ctypes.c_int, vp]
         L.wkv6_fwd_gn.restype = ctypes.c_int
@@ -95,6 +97,13 @@ def fwd_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, 
             y: int, mode: int, dtype: int, stream: int = 0) -> int:
     """Direct call with integer addresses; returns the status code."""
     return lib().wkv6_fwd(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype, stream)
+
+
+def fwd_noalloc_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, u: int,
+                    y: int, mode: int, dtype: int, stream: int = 0) -> int:
+    """Direct call of wkv6_fwd_noalloc (workspace in the library's static
+    scratch array) with integer addresses."""
+    return lib().wkv6_fwd_noalloc(B, T, C, H, r, k, v, w_raw, u, y, mode, dtype, stream)
 
 
 def fwd5_raw(B: int, T: int, C: int, H: int, r: int, k: int, v: int, w_raw: int, u: int,
@@ -219,6 +228,26 @@ def fwd(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
         _check_out(out, (B, T, C), torch.float32, r.device, "out")
     st = fwd_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
                  u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, _stream_handle(stream, r.device))
+    if st != OK:
+        raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
+    return out
+
+
+def fwd_noalloc(r, k, v, w_raw, u, H: int, mode: str = "causal", out=None, stream=None):
+    """fwd() through wkv6_fwd_noalloc: the library allocates nothing (segment
+    summaries go to its static per-device scratch array).  Calls that may
+    overlap on one GPU race on that array."""
+    import torch
+
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    B, T, C, dtype = _check_inputs(r, k, v, w_raw, u)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=r.device)
+    else:
+        _check_out(out, (B, T, C), torch.float32, r.device, "out")
+    st = fwd_noalloc_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(),
+                         u.data_ptr(), out.data_ptr(), _MODES[mode], dtype, _stream_handle(stream, r.device))
     if st != OK:
         raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
     return out
