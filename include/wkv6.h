@@ -34,13 +34,14 @@
 #ifndef WKV6_H
 #define WKV6_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define WKV6_ABI_VERSION 5
+#define WKV6_ABI_VERSION 6
 
 /* mode */
 #define WKV6_MODE_CAUSAL        0
@@ -82,11 +83,10 @@ extern "C" {
  * none of them after returning.  When B*H is small the library cuts each
  * sequence into segments handled by different workgroups (more when the
  * sequences are long enough); such calls take a temporary device workspace
- * of B*H*segments*2*(64*64+64)*4 bytes for the segment summaries, allocated
- * and released in stream order on `stream`, from a memory pool the library
- * creates on each device (hipMemPoolCreate) and that keeps freed blocks for
- * later calls until the process ends.
- * Other calls allocate nothing.  y is written in place while the call runs:
+ * of B*H*segments*2*(64*64+64)*4 bytes for the segment summaries
+ * (wkv6_fwd_workspace_bytes gives the exact figure), allocated and released
+ * in stream order on `stream` from the library's workspace pool (see
+ * WKV6_WORKSPACE_KEEP_BYTES below).  Other calls allocate nothing.  y is written in place while the call runs:
  * a bidirectional call first stores the later-token part of every row and
  * then adds the rest, so y must not be read before the stream has run the
  * call.
@@ -103,6 +103,34 @@ extern "C" {
 int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H,
              const void* r, const void* k, const void* v, const void* w_raw,
              const float* u, float* y, int mode, int dtype, void* stream);
+
+/*
+ * Workspace pool.  Calls that need device workspace (segmented calls, the
+ * backward, the bidirectional fused epilogue, segmented RWKV-4 calls) take it
+ * in stream order from a memory pool the library creates on each device on
+ * first use (hipMemPoolCreate).  Freed blocks stay in the pool for later
+ * calls up to WKV6_WORKSPACE_KEEP_BYTES per device; the runtime returns
+ * memory above that to the device when a stream or the device synchronises.
+ * This departs from a library that allocates nothing: the long sequences
+ * over few (batch, head) pairs need per-segment summaries, and allocating
+ * them from the default pool on every call cost 9-36 us.  Callers that
+ * cannot allocate use wkv6_fwd_noalloc.
+ */
+#define WKV6_WORKSPACE_KEEP_BYTES ((size_t)256 << 20)
+
+/* Bytes of workspace a wkv6_fwd call with these arguments takes from the pool
+ * (0: none, or the arguments are invalid).  Host arithmetic only: no device
+ * is touched. */
+size_t wkv6_fwd_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t H, int mode, int dtype);
+
+/* Bytes the current device's workspace pool holds now (in use and kept), or
+ * 0 if the library has not created it. */
+size_t wkv6_workspace_reserved_bytes(void);
+
+/* Hands every unused block of the current device's workspace pool back to
+ * the device (hipMemPoolTrimTo); blocks of calls still in flight are kept.
+ * Returns WKV6_OK or WKV6_ERR_HIP. */
+int wkv6_trim_workspace(void);
 
 /*
  * wkv6_fwd_noalloc -- wkv6_fwd for callers that cannot allocate device

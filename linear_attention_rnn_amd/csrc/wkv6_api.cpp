@@ -80,34 +80,42 @@ int check_tensors(int64_t B, int64_t T, int64_t C, int dtype, const void* r, con
 }
 
 // Workspace memory comes from a stream-ordered pool the library owns, one
-// per device, that keeps freed blocks for the next call instead of handing
-// them back: allocating from the default pool cost 9-36 us per call.
-hipError_t ws_alloc(void** p, size_t bytes, hipStream_t s) {
-  static std::mutex mu;
-  static std::vector<hipMemPool_t> pools;
+// per device (allocating from the default pool cost 9-36 us per call).  The
+// pool keeps up to WKV6_WORKSPACE_KEEP_BYTES of freed blocks for later calls;
+// the runtime hands anything above that back to the device at the next
+// synchronisation, and wkv6_trim_workspace releases the rest.
+std::mutex g_pool_mu;
+std::vector<hipMemPool_t> g_pools;
+
+// The current device's pool (created on first use when `create`), or null.
+hipError_t device_pool(hipMemPool_t* out, bool create) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  hipMemPool_t pool;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    if ((int)pools.size() <= dev) pools.resize(dev + 1, nullptr);
-    if (!pools[dev]) {
-      hipMemPoolProps props = {};
-      props.allocType = hipMemAllocationTypePinned;
-      props.location.type = hipMemLocationTypeDevice;
-      props.location.id = dev;
-      hipMemPool_t created = nullptr;
-      if ((e = hipMemPoolCreate(&created, &props)) != hipSuccess) return e;
-      uint64_t keep = UINT64_MAX;
-      if ((e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
-        hipMemPoolDestroy(created);   // a pool that hands blocks back would cost every call an allocation
-        return e;
-      }
-      pools[dev] = created;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if ((int)g_pools.size() <= dev) g_pools.resize(dev + 1, nullptr);
+  if (!g_pools[dev] && create) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t created = nullptr;
+    if ((e = hipMemPoolCreate(&created, &props)) != hipSuccess) return e;
+    uint64_t keep = WKV6_WORKSPACE_KEEP_BYTES;
+    if ((e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
+      (void)hipMemPoolDestroy(created);   // only a pool with the documented bound is kept
+      return e;
     }
-    pool = pools[dev];
+    g_pools[dev] = created;
   }
+  *out = g_pools[dev];
+  return hipSuccess;
+}
+
+hipError_t ws_alloc(void** p, size_t bytes, hipStream_t s) {
+  hipMemPool_t pool = nullptr;
+  const hipError_t e = device_pool(&pool, true);
+  if (e != hipSuccess) return e;
   return hipMallocFromPoolAsync(p, bytes, pool, s);
 }
 
@@ -168,6 +176,31 @@ const char* wkv6_status_str(int status) {
 }
 
 const char* wkv6_last_error(void) { return g_last_error.c_str(); }
+
+size_t wkv6_fwd_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t H, int mode, int dtype) {
+  g_last_error.clear();
+  if (check_sizes(B, T, C, H, mode, dtype) != WKV6_OK) return 0;
+  if (B == 0 || T == 0) return 0;
+  return wkv6::workspace_bytes(make_args(B, T, C, H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, mode,
+                                         dtype));
+}
+
+size_t wkv6_workspace_reserved_bytes(void) {
+  hipMemPool_t pool = nullptr;
+  if (device_pool(&pool, false) != hipSuccess || !pool) return 0;
+  uint64_t v = 0;
+  if (hipMemPoolGetAttribute(pool, hipMemPoolAttrReservedMemCurrent, &v) != hipSuccess) return 0;
+  return (size_t)v;
+}
+
+int wkv6_trim_workspace(void) {
+  g_last_error.clear();
+  hipMemPool_t pool = nullptr;
+  hipError_t e = device_pool(&pool, false);
+  if (e == hipSuccess && pool) e = hipMemPoolTrimTo(pool, 0);
+  if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("workspace trim: ") + hipGetErrorString(e));
+  return WKV6_OK;
+}
 
 int wkv6_fwd(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const void* k,
              const void* v, const void* w_raw, const float* u, float* y, int mode, int dtype,

@@ -77,8 +77,34 @@ def lib() -> ctypes.CDLL:
         L.wkv6_last_error.restype = ctypes.c_char_p
         L.wkv6_abi_version.argtypes = []
         L.wkv6_abi_version.restype = ctypes.c_int
+        L.wkv6_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+        L.wkv6_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.wkv6_workspace_reserved_bytes.argtypes = []
+        L.wkv6_workspace_reserved_bytes.restype = ctypes.c_size_t
+        L.wkv6_trim_workspace.argtypes = []
+        L.wkv6_trim_workspace.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+WORKSPACE_KEEP_BYTES = 256 << 20   # WKV6_WORKSPACE_KEEP_BYTES
+
+
+def fwd_workspace_bytes(B: int, T: int, C: int, H: int, mode: str = "causal", bf16: bool = True) -> int:
+    """Workspace bytes a wkv6_fwd call of these sizes takes (host arithmetic)."""
+    return lib().wkv6_fwd_workspace_bytes(B, T, C, H, _MODES[mode], DTYPE_BF16 if bf16 else DTYPE_F32)
+
+
+def workspace_reserved_bytes() -> int:
+    """Bytes the current device's workspace pool holds now."""
+    return lib().wkv6_workspace_reserved_bytes()
+
+
+def trim_workspace() -> None:
+    """Hand the unused blocks of the current device's workspace pool back."""
+    st = lib().wkv6_trim_workspace()
+    if st != OK:
+        raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
 
 
 def abi_version() -> int:

@@ -18,7 +18,7 @@ A = 0x10000  # fake, 16-byte aligned addresses: never dereferenced by these call
 
 def test_exports_every_declared_function():
     names = wkv6.header_functions()
-    assert set(names) == {"wkv6_fwd", "wkv6_fwd_noalloc", "wkv6_fwd_gn", "wkv5_fwd", "wkv4_fwd", "wkv6_fwd_state", "wkv6_bwd", "wkv6_status_str",
+    assert set(names) == {"wkv6_fwd", "wkv6_fwd_noalloc", "wkv6_fwd_workspace_bytes", "wkv6_workspace_reserved_bytes", "wkv6_trim_workspace", "wkv6_fwd_gn", "wkv5_fwd", "wkv4_fwd", "wkv6_fwd_state", "wkv6_bwd", "wkv6_status_str",
                           "wkv6_last_error", "wkv6_abi_version"}
     L = wkv6.lib()
     for n in names:
@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert wkv6.abi_version() == 5
+    assert wkv6.abi_version() == 6
     assert wkv6.status_str(0) == "ok"
     texts = {wkv6.status_str(s) for s in range(5)}
     assert len(texts) == 5
@@ -303,3 +303,28 @@ def test_gn_null_misaligned_overlap(which):
 def test_gn_empty_problem_is_a_noop():
     assert _call_gn(B=0, ptrs=[0] * 9) == wkv6.OK
     assert _call_gn(T=0, ptrs=[0] * 9) == wkv6.OK
+
+
+def test_fwd_workspace_bytes_follows_the_documented_formula():
+    """wkv6_fwd_workspace_bytes (host arithmetic, no GPU): zero for calls that
+    are not cut into segments (enough (batch, head) pairs, or at most four
+    causal tokens), else B*H*segments*2*(64*64+64)*4 bytes, as include/wkv6.h
+    documents, with 1 < segments <= the number of 64-token chunks."""
+    per = 2 * (64 * 64 + 64) * 4
+    assert wkv6.fwd_workspace_bytes(64, 196, 768, 12, "bidirectional") == 0   # image-base: 768 pairs
+    assert wkv6.fwd_workspace_bytes(8, 4, 2048, 32, "causal") == 0            # decode kernel
+    assert wkv6.fwd_workspace_bytes(-1, 4, 128, 2) == 0                       # invalid sizes
+    for B, T, C, H, mode, bf16 in ((8, 4096, 2048, 32, "causal", True), (4, 4096, 1024, 16, "bidirectional", True),
+                                   (1, 1000, 128, 2, "causal", False), (2, 587, 192, 3, "bidirectional", True)):
+        n = wkv6.fwd_workspace_bytes(B, T, C, H, mode, bf16)
+        assert n > 0 and n % (B * H * per) == 0, (B, T, n)
+        G = n // (B * H * per)
+        assert 1 < G <= (T + 63) // 64, (B, T, G)
+
+
+def test_workspace_keep_bound_matches_the_header():
+    import re
+
+    with open(wkv6.HEADER) as f:
+        m = re.search(r"#define WKV6_WORKSPACE_KEEP_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == wkv6.WORKSPACE_KEEP_BYTES == 256 << 20
