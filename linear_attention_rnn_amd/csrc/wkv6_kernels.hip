@@ -1506,6 +1506,196 @@ __global__ __launch_bounds__(NT, occupancy<BF16>()) void summary_both_kernel(Par
   }
 }
 
+// ---------------------------------------------------------------------------
+// Segment summaries with the state split by rows (bf16 inputs, per-token
+// decay).  The decay acts on the key channel c alone, so row c of a state
+// never mixes with another row: wave J owns rows c = 16J .. 16J + 15 of both
+// summaries for the whole segment, and the waves share nothing but the
+// staged input tiles.  Per 64-token chunk (tokens in order, t local):
+//   forward  S <- 2^Ltot S + sum_t (k_t 2^(Ltot - Lin_t))^T v_t
+//   reverse  R <- R + sum_t (k_t 2^(P + Lex_t))^T v_t   (P: the segment's
+//            decay before the chunk, so 2^(P + Lex_t) is the decay of the
+//            segment's tokens before t)
+// Every factor is at most 1, so no range guard or slow path is needed.  The
+// products run as S^T[n][c] += sum_t V[t][n] eta[t][c] on MFMA: lane (g, i)
+// of wave J holds channel c = 16J + i in all four accumulator tiles, so the
+// per-channel row scaling 2^Ltot is a per-lane factor, and its operand slots
+// (tokens 8g .. 8g + 7 of k-step ks) are where it scans lambda, in
+// registers.  The k, v and w tiles are staged row-major in swizzled LDS
+// planes (two buffers), read down their columns with transposed LDS reads;
+// the next chunk's loads are issued as soon as the current chunk is staged,
+// so they are in flight for a whole chunk step, and one barrier per chunk
+// orders the staging.
+//   BOTH: also the reverse summary (bidirectional calls); else the forward
+//         one of every segment but the last (causal calls).
+struct RowSummLds {
+  static constexpr int kTile = PL * 2;            // one 64 x 64 bf16 plane
+  static constexpr int kBuf = 3 * kTile;          // k, v, w
+  static constexpr int kBytes = 2 * kBuf;         // two buffers
+};
+
+// Offsets of the transposed column reads of column block cb (as LdsOff::kt).
+__device__ __forceinline__ void col_offsets(int cb, int g, int li, int (&kt)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int m = (li >> 2) + 4 * h, q = li & 3;
+    kt[h] = (8 * g + m) * 64 + (((2 * cb + (q >> 1)) ^ m) << 3) + 4 * (q & 1);
+  }
+}
+
+// bf16x8 operand of 8 consecutive tokens (down a column) as floats.
+__device__ __forceinline__ void widen8(const bf16x8& x, float (&o)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = (float)x[j];
+}
+
+template <bool BOTH>
+__global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char lds[RowSummLds::kBytes];
+  const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
+  if (!BOTH && seg == p.G - 1) return;   // no later segment needs it
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int J = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  const int b = bh / p.H, h = bh % p.H;
+  const int64_t T = p.T, C = p.C;
+  const int64_t base = (int64_t)b * T * C + (int64_t)h * HS;
+  const int64_t t_lo = (int64_t)seg * p.SEGC * LC;
+  const int64_t n = min(T, t_lo + (int64_t)p.SEGC * LC) - t_lo;
+  const int nch = (int)((n + LC - 1) / LC);
+  const Rsrc rk = slice_rsrc(p.k, base, 2, T, C), rv = slice_rsrc(p.v, base, 2, T, C);
+  const Rsrc rw = slice_rsrc(p.w, base, 2, T, C);
+
+  // staging: thread tid moves 16-byte pieces tid and tid + 256 of each tile
+  // (row = piece / 8, 8-channel column group = piece % 8)
+  int srow[2], scol[2], sdst[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int pc = tid + 256 * hh;
+    srow[hh] = pc >> 3;
+    scol[hh] = pc & 7;
+    sdst[hh] = swz(srow[hh], 8 * scol[hh]);
+  }
+  const uint32_t row0 = (uint32_t)t_lo * (uint32_t)C * 2u, rstep = (uint32_t)C * 2u;
+  uint4 stg[3][2];
+  auto fetch = [&](int ch) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int t = ch * LC + srow[hh];   // rows past the segment read zero
+      const int off = t < n ? (int)(row0 + (uint32_t)t * rstep) + 16 * scol[hh] : kOffNone;
+      stg[0][hh] = bload16(rk, off);
+      stg[1][hh] = bload16(rv, off);
+      stg[2][hh] = bload16(rw, off);
+    }
+  };
+  int ktJ[2], ktV[4][2];
+  col_offsets(J, g, li, ktJ);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) col_offsets(nt, g, li, ktV[nt]);
+
+  f32x4 S[4], R[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    R[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float P = 0.f;   // the segment's log2 decay before the chunk, channel 16J + li
+  const bool odd = (g & 1) != 0, upper = (g & 2) != 0;
+
+  auto step = [&](int ch) {
+    char* buf = lds + (ch & 1) * RowSummLds::kBuf;
+    // stage this chunk, then send the next chunk's loads out at once
+#pragma unroll
+    for (int ti = 0; ti < 3; ++ti)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        *reinterpret_cast<uint4*>(buf + ti * RowSummLds::kTile + 2 * sdst[hh]) = stg[ti][hh];
+    if (ch + 1 < nch) fetch(ch + 1);
+    lds_barrier();   // (the other buffer's readers finished before the previous barrier)
+    const __bf16* sK = reinterpret_cast<const __bf16*>(buf);
+    const __bf16* sV = reinterpret_cast<const __bf16*>(buf + RowSummLds::kTile);
+    const __bf16* sW = reinterpret_cast<const __bf16*>(buf + 2 * RowSummLds::kTile);
+    const int Lv = (int)min<int64_t>(LC, n - (int64_t)ch * LC);
+
+    // lambda's inclusive (Lin) and exclusive (Lex) prefix over the chunk for
+    // tokens 32 ks + 8 g + j of channel 16J + li (tokens past the segment
+    // have lambda = 0)
+    float lin[2][8], lex[2][8], tot = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float w8[8];
+      widen8(rdcol8<1>(sW, ktJ, 2048 * ks).p[0], w8);
+      float run = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = 32 * ks + 8 * g + j;
+        const float lam = t < Lv ? -kLog2e * ex2(w8[j] * kLog2e) : 0.f;
+        lex[ks][j] = run;
+        run += lam;
+        lin[ks][j] = run;
+      }
+      // exclusive prefix of the four 8-token groups: rows g of the wave hold
+      // the groups of one channel (permlane swaps with the row g ^ 1, g ^ 2)
+      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(run), __float_as_uint(run), false, false);
+      const float partner = __uint_as_float(odd ? a[0] : a[1]);
+      const float pair = run + partner;
+      const auto c2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+      const float other = __uint_as_float(upper ? c2[0] : c2[1]);
+      const float pre = tot + (odd ? partner : 0.f) + (upper ? other : 0.f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lin[ks][j] += pre;
+        lex[ks][j] += pre;
+      }
+      tot += pair + other;
+    }
+
+    // S <- 2^tot S + (k 2^(tot - Lin))^T V;  R <- R + (k 2^(P + Lex))^T V.
+    // The accumulator entries of a lane all belong to its channel, so the
+    // decay is one factor per lane.
+    const float dec = ex2(tot);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[nt][j] *= dec;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (32 * ks >= Lv) break;
+      float k8[8], ef[8], er[8];
+      widen8(rdcol8<1>(sK, ktJ, 2048 * ks).p[0], k8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ef[j] = k8[j] * ex2(tot - lin[ks][j]);
+        if (BOTH) er[j] = k8[j] * ex2(P + lex[ks][j]);
+      }
+      const Op<2> eo = split8<2>(ef);
+      Op<2> ro;
+      if (BOTH) ro = split8<2>(er);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const Op<1> vt = rdcol8<1>(sV, ktV[nt], 2048 * ks);
+        S[nt] = mma(vt, eo, S[nt]);
+        if (BOTH) R[nt] = mma(vt, ro, R[nt]);
+      }
+    }
+    P += tot;
+  };
+  fetch(0);
+  for (int ch = 0; ch < nch; ++ch) step(ch);
+
+  // S^T[n][c] (and R^T) with n = 16 nt + 4g + j, c = 16J + li; the segment's
+  // total log2 decay of channel 16J + li from the lanes of row 0
+#pragma unroll
+  for (int d = 0; d < (BOTH ? 2 : 1); ++d) {
+    float* dst = p.summ + (((int64_t)bh * p.G + seg) * 2 + d) * kSummFloats;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[(16 * nt + 4 * g + j) * HS + 16 * J + li] = d == 0 ? S[nt][j] : R[nt][j];
+    if (g == 0) dst[PL + 16 * J + li] = P;
+  }
+}
+
 // State passing through an empty sequence: s_out = s_in (zero without s_in).
 __global__ __launch_bounds__(NT) void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                                        int64_t n) {
@@ -1691,7 +1881,9 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   hipError_t e;
   if (pl.G > 1) {
     const dim3 sgrid(bh * pl.G);
-    if constexpr (BIDIR)
+    if constexpr (BF16 && !WS)   // per-token decays from bf16 rows: the row-split summaries
+      hipLaunchKernelGGL((summary_rows_kernel<BIDIR>), sgrid, block, 0, s, p);
+    else if constexpr (BIDIR)
       hipLaunchKernelGGL((summary_both_kernel<BF16, WS>), sgrid, block, 0, s, p);
     else
       hipLaunchKernelGGL((summary_kernel<BF16, WS>), sgrid, block, 0, s, p);
