@@ -24,6 +24,9 @@ Prints ONE JSON line (rank 0) with, besides the throughput:
              the algorithmic flops (12 N^2 per token, head and direction)
   wkv6_fwd_gn  the forward with the per-head group normalisation, affine and
              gate fused into its output (bf16 out; y never written)
+  wkv6_fwd_then_gn  the same result in the unfused order: wkv6_fwd, then
+             wkv6_group_norm_gate on its y (same algorithmic bytes as the
+             fused op, so the two lines compare call times directly)
   wkv5_fwd   RWKV-5: the forward with one decay per channel for every token
   wkv4_fwd   RWKV-4: the normalised per-channel operator (always causal)
 """
@@ -48,7 +51,7 @@ HEADLINE = "text-long-causal-bf16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak, published
-OPS = ("wkv6_fwd", "wkv6_bwd", "wkv6_fwd_gn", "wkv5_fwd", "wkv4_fwd")
+OPS = ("wkv6_fwd", "wkv6_bwd", "wkv6_fwd_gn", "wkv6_fwd_then_gn", "wkv5_fwd", "wkv4_fwd")
 MALL_BYTES = 256 << 20
 MFMA_FLOPS = 2 * 16 * 16 * 32  # one v_mfma_f32_16x16x32_bf16
 METRIC = "WKV6 fwd tokens/s (B·T/s) + % HBM roofline & MFMA util at N=64, 1 GPU"
@@ -158,7 +161,7 @@ def cpu_baseline(w: I.Workload, x: dict, budget_s: float = 20.0, op: str = "wkv6
         elif op == "wkv6_bwd":
             oracle.wkv6_ref_backward(x["r"][:nb], x["k"][:nb], x["v"][:nb], x["w_raw"][:nb], x["u"],
                                      x["dy"][:nb], w.H, w.mode)
-        elif op == "wkv6_fwd_gn":
+        elif op in ("wkv6_fwd_gn", "wkv6_fwd_then_gn"):
             oracle.wkv6_gn_ref(x["r"][:nb], x["k"][:nb], x["v"][:nb], x["w_raw"][:nb], x["u"], x["g"][:nb],
                                x["gamma"], x["beta"], 64e-5, w.H, w.mode)
         elif op == "wkv5_fwd":
@@ -256,7 +259,7 @@ def main() -> int:
         x["dy"] = np.random.default_rng(w.seed + 1000).normal(0.0, 0.5, size=(w.B, w.T, w.C)).astype(np.float32)
         # read r, k, v, w_raw, dy and u; write dr, dk, dv, dw_raw and du
         per_copy = E * (4 * isz + 4 + 16) + 2 * w.C * 4
-    elif op == "wkv6_fwd_gn":
+    elif op in ("wkv6_fwd_gn", "wkv6_fwd_then_gn"):
         x = I.make_inputs(w)
         rng = np.random.default_rng(w.seed + 2000)
         x["g"] = rng.normal(size=(w.B, w.T, w.C)).astype(np.float32)
@@ -281,10 +284,12 @@ def main() -> int:
             d = [dev(x[key], w.dtype) for key in ("r", "k", "v", "w_raw")] + [f32(x["u"])]
         if op == "wkv6_bwd":
             d.append(f32(x["dy"]))
-        if op == "wkv6_fwd_gn":
+        if op in ("wkv6_fwd_gn", "wkv6_fwd_then_gn"):
             d += [dev(x["g"], w.dtype), f32(x["gamma"]), f32(x["beta"])]
-        y = torch.empty((w.B, w.T, w.C), dtype=torch.bfloat16 if op == "wkv6_fwd_gn" else torch.float32,
-                        device="cuda") if op != "wkv6_bwd" else None
+        y = torch.empty((w.B, w.T, w.C), dtype=torch.bfloat16 if op in ("wkv6_fwd_gn", "wkv6_fwd_then_gn")
+                        else torch.float32, device="cuda") if op != "wkv6_bwd" else None
+        if op == "wkv6_fwd_then_gn":   # the forward's y between the two passes
+            d.append(torch.empty((w.B, w.T, w.C), dtype=torch.float32, device="cuda"))
         sets.append((d, y))
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -297,6 +302,10 @@ def main() -> int:
             wkv6.bwd(*d, w.H, w.mode, stream=stream)
         elif op == "wkv6_fwd_gn":
             wkv6.fwd_gn(*d, w.H, w.mode, out=y, stream=stream)
+        elif op == "wkv6_fwd_then_gn":
+            r_, k_, v_, w_, u_, g_, ga_, be_, ybuf = d
+            wkv6.fwd(r_, k_, v_, w_, u_, w.H, w.mode, out=ybuf, stream=stream)
+            wkv6.group_norm_gate(ybuf, g_, ga_, be_, w.H, eps=64e-5, out=y, stream=stream)
         elif op == "wkv5_fwd":
             wkv6.fwd5(*d, w.H, w.mode, out=y, stream=stream)
         else:
@@ -321,7 +330,7 @@ def main() -> int:
 
     alg_bytes = per_copy
     achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
-    forward6 = op in ("wkv6_fwd", "wkv6_fwd_gn", "wkv5_fwd")   # the chunked MFMA kernels
+    forward6 = op in ("wkv6_fwd", "wkv6_fwd_gn", "wkv6_fwd_then_gn", "wkv5_fwd")   # the chunked MFMA kernels
     n_mfma = mfma_count(w) if forward6 else 0
     mfma_tflops = n_mfma * MFMA_FLOPS / (mean_ms * 1e-3) / 1e12
     traffic = traffic_record(w.name) if op == "wkv6_fwd" else None
@@ -339,6 +348,7 @@ def main() -> int:
     else:
         kern = {"wkv6_fwd": "wkv6_fwd call: fast-path sweep kernel + fix-up kernel",
                 "wkv6_fwd_gn": "wkv6_fwd_gn call: fast-path sweep kernel with the fused epilogue + fix-up kernel",
+                "wkv6_fwd_then_gn": "wkv6_fwd call, then wkv6_group_norm_gate on its y (the unfused order)",
                 "wkv5_fwd": "wkv5_fwd call: fast-path sweep kernel + fix-up kernel",
                 "wkv4_fwd": "wkv4_fwd call: per-channel recurrence kernels"}[op]
         if forward6 and plan_segments(w)[0] > 1:
@@ -363,7 +373,7 @@ def main() -> int:
         "data": "synthetic (seeded numpy draws, recipe in linear_attention_rnn_amd/inputs.py)",
         "config": {"workload": w.name, "op": op, "mode": mode, "B": w.B, "T": w.T, "C": w.C, "H": w.H,
                    "N": w.N, "inputs": w.dtype,
-                   "state_and_output": "f32 state, bf16 output" if op == "wkv6_fwd_gn" else "f32",
+                   "state_and_output": "f32 state, bf16 output" if op in ("wkv6_fwd_gn", "wkv6_fwd_then_gn") else "f32",
                    "rotating_copies": ncopy, "parallelism": "single GPU"},
         "roofline": roofline,
     }

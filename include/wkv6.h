@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define WKV6_ABI_VERSION 6
+#define WKV6_ABI_VERSION 7
 
 /* mode */
 #define WKV6_MODE_CAUSAL        0
@@ -191,6 +191,30 @@ int wkv6_fwd_gn(int64_t B, int64_t T, int64_t C, int64_t H,
                 const void* r, const void* k, const void* v, const void* w_raw,
                 const float* u, const void* g, const float* gamma, const float* beta,
                 float eps, void* out, int mode, int dtype, void* stream);
+
+/*
+ * wkv6_group_norm_gate -- the output normalisation and gate of wkv6_fwd_gn as
+ * a pass of its own over a y already in memory (the unfused order: any
+ * forward entry point, then this one):
+ *
+ *   out[b,t,c] = ( (y[b,t,c] - mean_h) / sqrt(var_h + eps) * gamma[c] + beta[c] ) * g[b,t,c]
+ *
+ * with the same readings as wkv6_fwd_gn (one group per head of 64 channels,
+ * biased variance, eps inside the root, g after its SiLU).
+ *
+ *   B, T, C, H    as wkv6_fwd (C = 64 * H)
+ *   y       device pointer to [B, T, C] float32
+ *   g       device pointer to [B, T, C] values of `dtype`
+ *   gamma, beta   device pointers to C float32 values each
+ *   eps     finite and >= 0 (else INVALID_ARG)
+ *   out     device pointer to a [B, T, C] bfloat16 output (nearest even);
+ *           must not overlap any input
+ *
+ * Allocates nothing; execution and errors as wkv6_fwd.
+ */
+int wkv6_group_norm_gate(int64_t B, int64_t T, int64_t C, int64_t H, const float* y, const void* g,
+                         const float* gamma, const float* beta, float eps, void* out, int dtype,
+                         void* stream);
 
 /*
  * wkv5_fwd -- the RWKV-5 ("Eagle") operator: the same matrix-state recurrence

@@ -304,6 +304,40 @@ int wkv6_fwd_gn(int64_t B, int64_t T, int64_t C, int64_t H, const void* r, const
   return run(a, static_cast<hipStream_t>(stream));
 }
 
+int wkv6_group_norm_gate(int64_t B, int64_t T, int64_t C, int64_t H, const float* y, const void* g,
+                         const float* gamma, const float* beta, float eps, void* out, int dtype, void* stream) {
+  g_last_error.clear();
+  int st = check_sizes(B, T, C, H, WKV6_MODE_CAUSAL, dtype);
+  if (st != WKV6_OK || B == 0 || T == 0) return st;
+  if (!(std::isfinite(eps) && eps >= 0.f)) return fail(WKV6_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const void* ptrs[5] = {y, g, gamma, beta, out};
+  const char* names[5] = {"y", "g", "gamma", "beta", "out"};
+  for (int i = 0; i < 5; ++i)
+    if (!ptrs[i]) return fail(WKV6_ERR_INVALID_ARG, std::string("null pointer: ") + names[i]);
+  for (int i = 0; i < 5; ++i)
+    if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16)
+      return fail(WKV6_ERR_MISALIGNED, std::string("pointer not 16-byte aligned: ") + names[i]);
+  const size_t elems = (size_t)B * (size_t)T * (size_t)C, isz = dtype == WKV6_DTYPE_BF16 ? 2 : 4;
+  const size_t nb[4] = {elems * 4, elems * isz, (size_t)C * 4, (size_t)C * 4};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(out, elems * 2, ptrs[i], nb[i]))
+      return fail(WKV6_ERR_INVALID_ARG, std::string("out overlaps ") + names[i]);
+  wkv6::GnArgs a;
+  a.B = B;
+  a.T = T;
+  a.C = C;
+  a.y = y;
+  a.g = g;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.eps = eps;
+  a.out = static_cast<uint16_t*>(out);
+  a.bf16 = dtype == WKV6_DTYPE_BF16;
+  const hipError_t e = wkv6::enqueue_gn_gate(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WKV6_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return WKV6_OK;
+}
+
 int wkv4_fwd(int64_t B, int64_t T, int64_t C, const void* k, const void* v, const float* w, const float* u,
              float* y, int dtype, void* stream) {
   g_last_error.clear();

@@ -75,6 +75,20 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(const BwdArgs& a);
 hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
 
+// Per-head group normalisation, affine and gate of a y in memory
+// (wkv6_groupnorm.hip): out = ((y - mean) * rstd * gamma + beta) * g, bf16.
+struct GnArgs {
+  int64_t B, T, C;
+  const float* y;       // [B, T, C] float32
+  const void* g;        // [B, T, C], float32 or bfloat16
+  const float* gamma;   // [C]
+  const float* beta;    // [C]
+  float eps;
+  uint16_t* out;        // [B, T, C] bfloat16
+  bool bf16;
+};
+hipError_t enqueue_gn_gate(const GnArgs& a, hipStream_t stream);
+
 // RWKV-4 (wkv4_kernels.hip): per-channel normalised WKV, causal.
 struct Wkv4Args {
   int64_t B, T, C;

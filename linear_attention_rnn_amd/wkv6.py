@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.wkv6_fwd_gn.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                   ctypes.c_int, ctypes.c_int, vp]
         L.wkv6_fwd_gn.restype = ctypes.c_int
+        L.wkv6_group_norm_gate.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int, vp]
+        L.wkv6_group_norm_gate.restype = ctypes.c_int
         L.wkv4_fwd.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, ctypes.c_int, vp]
         L.wkv4_fwd.restype = ctypes.c_int
         L.wkv6_fwd_state.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -323,6 +325,36 @@ def fwd_gn(r, k, v, w_raw, u, g, gamma, beta, H: int, mode: str = "causal", eps:
     st = fwd_gn_raw(B, T, C, H, r.data_ptr(), k.data_ptr(), v.data_ptr(), w_raw.data_ptr(), u.data_ptr(),
                     g.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps), out.data_ptr(), _MODES[mode],
                     dtype, _stream_handle(stream, r.device))
+    if st != OK:
+        raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
+    return out
+
+
+def group_norm_gate(y, g, gamma, beta, H: int, eps: float = 64e-5, out=None, stream=None):
+    """bf16 [B, T, C] = (GroupNorm over each head's 64 channels of y) * gamma
+    + beta, times the gate g: the epilogue of fwd_gn as a pass of its own.
+    y: float32 [B, T, C]; g: [B, T, C] float32 or bfloat16; gamma, beta:
+    float32 [C]."""
+    import torch
+
+    if y.dim() != 3 or y.dtype != torch.float32:
+        raise ValueError("y must be a float32 [B, T, C] tensor")
+    B, T, C = y.shape
+    if g.shape != y.shape or g.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("g must be [B, T, C] float32 or bfloat16")
+    for name, t in (("y", y), ("g", g)):
+        if not t.is_cuda or not t.is_contiguous() or t.device != y.device:
+            raise ValueError(f"{name} must be a contiguous tensor on y's GPU")
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t.dtype != torch.float32 or t.numel() != C or not t.is_cuda or not t.is_contiguous() or t.device != y.device:
+            raise ValueError(f"{name} must be a contiguous float32 tensor of C values on y's GPU")
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.bfloat16, device=y.device)
+    else:
+        _check_out(out, (B, T, C), torch.bfloat16, y.device, "out")
+    dtype = DTYPE_BF16 if g.dtype == torch.bfloat16 else DTYPE_F32
+    st = lib().wkv6_group_norm_gate(B, T, C, H, y.data_ptr(), g.data_ptr(), gamma.data_ptr(), beta.data_ptr(),
+                                    float(eps), out.data_ptr(), dtype, _stream_handle(stream, y.device))
     if st != OK:
         raise WKV6Error(st, f"{status_str(st)}: {last_error()}")
     return out

@@ -104,6 +104,14 @@ int main() {
            WKV6_ERR_INVALID_ARG);
   REJECT(wkv6_fwd_gn(2, 8, 128, 2, P(0), P(1), P(2), P(3), F(4), P(5), F(6), F(7), 1e-5f, P(5), 1, 1, nullptr),
          WKV6_ERR_INVALID_ARG);   // out overlaps g
+  // standalone normalisation and gate
+  for (float e : bad_eps)
+    REJECT(wkv6_group_norm_gate(2, 8, 128, 2, F(0), P(1), F(2), F(3), e, P(4), 1, nullptr), WKV6_ERR_INVALID_ARG);
+  REJECT(wkv6_group_norm_gate(2, 8, 128, 2, F(0), P(1), F(2), F(3), 1e-5f, P(0), 1, nullptr), WKV6_ERR_INVALID_ARG);
+  REJECT(wkv6_group_norm_gate(2, 8, 96, 2, F(0), P(1), F(2), F(3), 1e-5f, P(4), 1, nullptr), WKV6_ERR_UNSUPPORTED);
+  before = g_enqueued;
+  EXPECT(wkv6_group_norm_gate(2, 8, 128, 2, F(0), P(1), F(2), F(3), 1e-5f, P(4), 0, nullptr) == WKV6_OK &&
+         g_enqueued == before + 1);
   // RWKV-4
   REJECT(wkv4_fwd(-2, 8, 128, P(0), P(1), F(2), F(3), F(4), 1, nullptr), WKV6_ERR_INVALID_ARG);
   REJECT(wkv4_fwd(2, 8, 128, P(0), P(1), F(2), F(3), F(4), 3, nullptr), WKV6_ERR_INVALID_ARG);

@@ -21,6 +21,10 @@ hipError_t enqueue_bwd(const BwdArgs&, void*, hipStream_t) {
   ++g_enqueued;
   return hipSuccess;
 }
+hipError_t enqueue_gn_gate(const GnArgs&, hipStream_t) {
+  ++g_enqueued;
+  return hipSuccess;
+}
 size_t wkv4_workspace_bytes(const Wkv4Args&) { return 0; }
 hipError_t enqueue_wkv4(const Wkv4Args&, void*, hipStream_t) {
   ++g_enqueued;

@@ -18,7 +18,7 @@ A = 0x10000  # fake, 16-byte aligned addresses: never dereferenced by these call
 
 def test_exports_every_declared_function():
     names = wkv6.header_functions()
-    assert set(names) == {"wkv6_fwd", "wkv6_fwd_noalloc", "wkv6_fwd_workspace_bytes", "wkv6_workspace_reserved_bytes", "wkv6_trim_workspace", "wkv6_fwd_gn", "wkv5_fwd", "wkv4_fwd", "wkv6_fwd_state", "wkv6_bwd", "wkv6_status_str",
+    assert set(names) == {"wkv6_fwd", "wkv6_fwd_noalloc", "wkv6_group_norm_gate", "wkv6_fwd_workspace_bytes", "wkv6_workspace_reserved_bytes", "wkv6_trim_workspace", "wkv6_fwd_gn", "wkv5_fwd", "wkv4_fwd", "wkv6_fwd_state", "wkv6_bwd", "wkv6_status_str",
                           "wkv6_last_error", "wkv6_abi_version"}
     L = wkv6.lib()
     for n in names:
@@ -27,7 +27,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert wkv6.abi_version() == 6
+    assert wkv6.abi_version() == 7
     assert wkv6.status_str(0) == "ok"
     texts = {wkv6.status_str(s) for s in range(5)}
     assert len(texts) == 5

@@ -144,6 +144,52 @@ def test_gn_zero_eps_and_constant_rows(torch_cuda):
     assert np.array_equal(out, want)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_group_norm_gate_standalone(torch_cuda, dtype):
+    """wkv6_group_norm_gate on a given y: the oracle's normalisation and gate
+    of that same y, within bf16 rounding of the result (2^-8 of its size)
+    plus float32 rounding of the row statistics."""
+    torch = torch_cuda
+    from linear_attention_rnn_amd import wkv6
+
+    B, T, H = 3, 77, 5
+    C = 64 * H
+    rng = np.random.default_rng(760)
+    y = (rng.normal(size=(B, T, C)) * rng.uniform(0.01, 30.0, size=(B, T, 1))
+         + rng.normal(size=(B, T, 1))).astype(np.float32)
+    g, gamma, beta = extras(B, T, C, 761, dtype)
+    out = wkv6.group_norm_gate(torch.from_numpy(y).cuda(), to_device(g, dtype), torch.from_numpy(gamma).cuda(),
+                               torch.from_numpy(beta).cuda(), H, eps=EPS)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    yh = y.astype(np.float64).reshape(B, T, H, 64)
+    z = ((yh - yh.mean(-1, keepdims=True)) / np.sqrt(yh.var(-1, keepdims=True) + EPS)).reshape(B, T, C)
+    ref = (z * gamma + beta) * g
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * (np.abs(gamma * g) * (1.0 + np.abs(z)) + np.abs(beta * g))
+    ratio = float(np.max(np.abs(got - ref) / bound))
+    say(f"[gn] standalone {dtype}: max err/bound {ratio:.3f}")
+    assert ratio <= 1.0
+
+
+@pytest.mark.parametrize("mode", ["causal", "bidirectional"])
+def test_forward_then_group_norm_gate(torch_cuda, mode):
+    """The unfused order (wkv6_fwd, then wkv6_group_norm_gate on its y) meets
+    the fused epilogue's bound against the oracle."""
+    torch = torch_cuda
+    from linear_attention_rnn_amd import wkv6
+
+    B, H, T = 2, 3, 300
+    C = 64 * H
+    x = I.random_inputs(B, T, C, H, seed=770, dtype="bf16")
+    g, gamma, beta = extras(B, T, C, 771, "bf16")
+    d = device_inputs(x, "bf16")
+    y = wkv6.fwd(*d, H, mode)
+    out = wkv6.group_norm_gate(y, to_device(g, "bf16"), torch.from_numpy(gamma).cuda(), torch.from_numpy(beta).cuda(),
+                               H, eps=EPS)
+    torch.cuda.synchronize()
+    check(f"two-step {mode}", x, g, gamma, beta, H, mode, "bf16", out.float().cpu().numpy().astype(np.float64))
+
+
 def test_gn_empty(torch_cuda):
     torch = torch_cuda
     from linear_attention_rnn_amd import wkv6
