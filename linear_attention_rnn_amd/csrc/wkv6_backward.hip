@@ -77,6 +77,7 @@ struct BwdParams {
   float* Sin;   // state entering the segment (from the earlier segments)
   float* Gin;   // adjoint after the segment's last token (from the later segments)
   float* sig;   // per channel: sum over the segment of r dr - k dk
+  const int* only;   // if set, only items with a nonzero entry run (the others return at once)
 };
 
 // Four consecutive channels of one input row, widened to float32.
@@ -217,6 +218,7 @@ template <bool BF16, bool REV>
 __global__ __launch_bounds__(NT) void bwd_kernel(BwdParams p) {
   __shared__ Smem sm;
   const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
+  if (p.only != nullptr && p.only[bh] == 0) return;
   const int b = bh / p.H, h = bh % p.H;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // token steps: rows c0 .. c0 + 3 and columns n0 .. n0 + 3 of the state
@@ -533,6 +535,7 @@ template <bool BF16, bool REV>
 __global__ __launch_bounds__(NT) void bwd_summary_kernel(BwdParams p) {
   __shared__ SummSmem sm;
   const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
+  if (p.only != nullptr && p.only[bh] == 0) return;
   const int b = bh / p.H, h = bh % p.H;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // token steps: rows c0 .. c0 + 3 and columns n0 .. n0 + 3 of both summaries
@@ -814,8 +817,22 @@ BwdPlan bwd_plan(const BwdArgs& a) {
 }
 
 struct BwdWs {
-  size_t du, drtmp, dir[2], total;   // byte offsets; dir: carries of each direction
+  size_t du, drtmp, dir[2], sst, slow, total;   // byte offsets; dir: carries of each direction
 };
+
+// The chunked kernels take bf16 calls whose items run unsegmented, over at
+// least kChunkedMinT tokens: they run one workgroup per CU, so on short
+// sequences with many items (B64 T196 H12: 491 against 444 us) the
+// token-serial kernels, three workgroups per CU, are faster; over long ones
+// the chunked kernels are (B8 T4096 H32: 1.09 against 1.80 ms).
+// WKV6_BWD_CHUNKED=1 / 0 forces the choice for such calls.
+constexpr int64_t kChunkedMinT = 449;
+
+bool use_chunked(const BwdArgs& a, const BwdPlan& pl) {
+  if (!a.bf16 || pl.G != 1) return false;
+  if (const char* e = getenv("WKV6_BWD_CHUNKED")) return atoi(e) != 0;
+  return a.T >= kChunkedMinT;
+}
 
 size_t up256(size_t n) { return (n + 255) & ~size_t(255); }
 
@@ -830,6 +847,13 @@ BwdWs bwd_ws(const BwdArgs& a, const BwdPlan& pl) {
   for (int d = 0; d < 2; ++d) {
     w.dir[d] = n;
     if (d == 0 || a.bidirectional) n += up256(per);
+  }
+  w.sst = w.slow = n;
+  if (use_chunked(a, pl)) {
+    const size_t nch = (size_t)((a.T + 63) / 64);
+    n += up256((size_t)a.B * a.H * nch * NT * 16 * 4);
+    w.slow = n;
+    n += up256((size_t)a.B * a.H * 4);
   }
   w.total = n;
   return w;
@@ -900,6 +924,21 @@ hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t s) {
   const int64_t bh = a.B * a.H;
   const dim3 grid((unsigned)(bh * pl.G));
   hipError_t e;
+  if (use_chunked(a, pl)) {
+    // chunked kernels, then the token-serial ones for the items they flagged
+    int* slow = reinterpret_cast<int*>(ws + lay.slow);
+    float* sst = reinterpret_cast<float*>(ws + lay.sst);
+    for (int d = 0; d < (a.bidirectional ? 2 : 1); ++d)
+      if ((e = enqueue_bwd_chunked(a, p.du_part, sst, slow, d == 1, s)) != hipSuccess) return e;
+    p.only = slow;
+    for (int d = 0; d < (a.bidirectional ? 2 : 1); ++d) {
+      launch_bwd(a.bf16, d == 1, false, grid, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(du_reduce_kernel, dim3((unsigned)((a.C + HS - 1) / HS)), block, 0, s, p.du_part, a.du,
+                       (int64_t)a.B, (int64_t)a.C);
+    return hipGetLastError();
+  }
   float* sig[2] = {nullptr, nullptr};
   for (int d = 0; d < (a.bidirectional ? 2 : 1); ++d) {
     const bool rev = d == 1;

@@ -75,6 +75,14 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(const BwdArgs& a);
 hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
 
+// One direction of the chunked backward on MFMA (bf16 inputs, one workgroup
+// per (batch, head); wkv6_backward_chunked.hip): the chunk-entry states into
+// sst ([B*H][ceil(T/64)][256][16] floats), then the gradients; items that
+// need the general decay path are flagged in slow ([B*H]) and skipped.
+// rev: the reversed sweep of a bidirectional call (adds to the outputs).
+hipError_t enqueue_bwd_chunked(const BwdArgs& a, float* du_part, float* sst, int* slow, bool rev,
+                               hipStream_t stream);
+
 // Per-head group normalisation, affine and gate of a y in memory
 // (wkv6_groupnorm.hip): out = ((y - mean) * rstd * gamma + beta) * g, bf16.
 struct GnArgs {

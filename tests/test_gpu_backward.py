@@ -148,3 +148,13 @@ def test_backward_segments_decay_extremes(torch_cuda, monkeypatch, mode):
     for G in (1, 3):
         monkeypatch.setenv("WKV6_BWD_SEGMENTS", str(G))
         check(f"segments {G} extremes {mode}", x, dy, H, mode, "f32")
+
+
+def test_backward_text_long_full(torch_cuda):
+    """The benched text-long shape (B = 8, T = 4096, C = 2048, H = 32, causal,
+    bf16) with the planner's own choice (unsegmented, on the chunked MFMA
+    kernels), every gradient compared with the oracle over the whole tensor."""
+    w = I.workload("text-long-causal-bf16")
+    x = I.make_inputs(w)
+    say(f"[backward] text-long full: B={w.B} T={w.T} C={w.C} H={w.H}")
+    check("text-long full (default plan)", x, dy_of(x, w.seed + 1000), w.H, w.mode, w.dtype)
