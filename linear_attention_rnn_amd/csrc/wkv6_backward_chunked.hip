@@ -231,8 +231,9 @@ struct CbLds {
   static constexpr int kQS = kXT + 4 * 64 * 4;     // per wave: sum_t q_t (S_in dy_t) [4][64]
   static constexpr int kPend = kQS + 4 * 64 * 4;   // P at a chunk's end [2][64]
   static constexpr int kU = kPend + 2 * 64 * 4;    // u of the head [64]
-  static constexpr int kDU = kU + 64 * 4;          // u gradient per wave [4][64]
-  static constexpr int kBytes = kDU + 4 * 64 * 4;
+  static constexpr int kDU = kU + 64 * 4;          // u gradient per token block [4][64]
+  static constexpr int kPG = kDU + 4 * 64 * 4;     // <G', S_in> per column half [2][64]; sum r u k [2][64]
+  static constexpr int kBytes = kPG + 4 * 64 * 4;
 };
 
 // DPP: lane i of each 16-lane row receives lane i + N of the row (0 if none).
@@ -308,14 +309,21 @@ __device__ __forceinline__ void out4(Rsrc r, int off, float a, float b, float c,
   bstoref4(r, off, a, b, c, d);
 }
 
+// Workgroup of kernel B: 8 waves, two per token block.  Wave (J, H), J = 0..3,
+// H = 0..1, owns positions 16J..16J+15 and, of every output indexed by a
+// channel, the tiles 2H and 2H + 1 (channels 32H .. 32H + 31); the score-like
+// tiles both need are computed by both.
+constexpr int NTB = 512;
+
 // REV: the reversed sweep of a bidirectional call (no u term; outputs added).
 template <bool REV>
-__global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
+__global__ __launch_bounds__(NTB, 1) void bwd_chunk_kernel(CbParams p) {
   __shared__ __attribute__((aligned(16))) char lds[CbLds::kBytes];
   const int bh = blockIdx.x;
   if (p.slow[bh]) return;   // the token-serial kernels take this item
   const int tid = threadIdx.x, lane = tid & 63;
-  const int J = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int J = wv & 3, H = wv >> 2;
   const int g = lane >> 4, li = lane & 15;
   const int b = bh / p.H, h = bh % p.H;
   const int64_t T = p.T, C = p.C;
@@ -339,7 +347,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
   float* sPend = reinterpret_cast<float*>(lds + CbLds::kPend);
   float* sU = reinterpret_cast<float*>(lds + CbLds::kU);
   float* sDU = reinterpret_cast<float*>(lds + CbLds::kDU);
-  sDU[tid] = 0.f;
+  float* sPG = reinterpret_cast<float*>(lds + CbLds::kPG);
+  if (tid < 256) sDU[tid] = 0.f;
   if (tid < 64) {
     sU[tid] = REV ? 0.f : p.u[h * HS + tid];
     sPend[64 * ((nch - 1) & 1) + tid] = 0.f;   // after the last chunk the adjoint is zero
@@ -356,18 +365,19 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
     const int64_t s = (int64_t)m * LC + pos;
     return s < T ? (int)((uint32_t)(REV ? T - 1 - s : s) * rstep4) : kOffNone;
   };
-  // the lane's inputs of one token: r, k, w at its channels 16 ct + 4 g + j,
-  // v and dy at channels 32 ks + 8 g + j; the chunk's S_in in lane order
-  u32x2 nr[4], nk[4], nw[4];
+  // the lane's inputs of one token: r, k, w at its channels 16 (2H + cl) + 4 g
+  // + j, v and dy at channels 32 ks + 8 g + j; its half of the chunk's S_in
+  u32x2 nr[2], nk[2], nw[2];
   uint4 nv[2];
-  float4 ndy[4], ns[4];
+  float4 ndy[4], ns[2];
   auto fetch_in = [&](int m) {
     const int o2 = row2(m), o4 = row4(m);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      nr[ct] = bload8(rr, o2 + 32 * ct + 8 * g);
-      nk[ct] = bload8(rk, o2 + 32 * ct + 8 * g);
-      nw[ct] = bload8(rw, o2 + 32 * ct + 8 * g);
+    for (int cl = 0; cl < 2; ++cl) {
+      const int o = o2 + 32 * (2 * H + cl) + 8 * g;
+      nr[cl] = bload8(rr, o);
+      nk[cl] = bload8(rk, o);
+      nw[cl] = bload8(rw, o);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -377,21 +387,26 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
     }
   };
   auto fetch_s = [&](int m) {
-    const float4* src = reinterpret_cast<const float4*>(p.sst + (((int64_t)bh * nch + m) * NT + tid) * 16);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) ns[nt] = src[nt];
+    const float4* src =
+        reinterpret_cast<const float4*>(p.sst + (((int64_t)bh * nch + m) * NT + 64 * J + lane) * 16 + 8 * H);
+    ns[0] = src[0];
+    ns[1] = src[1];
   };
 
-  int kpi[4][2], ksg[4][2];
+  // transposed-read offsets: pi order at the column blocks 2H, 2H + 1 (kap^T,
+  // q^T, dy^T, G'^T operands), sigma order at blocks 2H, 2H + 1 and J (the
+  // adjoint update)
+  int kpi[2][2], ksg[2][2], ksj[2];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    colpi_offsets(16 * x, g, li, kpi[x]);
-    col_offsets(x, g, li, ksg[x]);
+  for (int x = 0; x < 2; ++x) {
+    colpi_offsets(16 * (2 * H + x), g, li, kpi[x]);
+    col_offsets(2 * H + x, g, li, ksg[x]);
   }
+  col_offsets(J, g, li, ksj);
 
-  f32x4 Gc[4];   // adjoint, lane: G[c = 16J + li][n = 16 nt + 4 g + j]
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) Gc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 Gc[2];   // adjoint, lane: G[c = 16J + li][n = 16 (2H + nl) + 4 g + j]
+  Gc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Gc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   fetch_in(nch - 1);
   fetch_s(nch - 1);
@@ -400,17 +415,17 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
     const bool valid = pos < Lv;
     const int o4 = row4(m);
     // ---- this chunk's raw values, then the next chunk's loads
-    u32x2 cr[4], ck[4];
-    float lam[4][4], dyf[2][8];
+    u32x2 cr[2], ck[2];
+    float lam[2][4], dyf[2][8];
     uint4 vq[2];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      cr[ct] = nr[ct];
-      ck[ct] = nk[ct];
+    for (int cl = 0; cl < 2; ++cl) {
+      cr[cl] = nr[cl];
+      ck[cl] = nk[cl];
       float w4[4];
-      bf4(nw[ct], w4);
+      bf4(nw[cl], w4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) lam[ct][j] = valid ? -kLog2e * ex2(w4[j] * kLog2e) : 0.f;
+      for (int j = 0; j < 4; ++j) lam[cl][j] = valid ? -kLog2e * ex2(w4[j] * kLog2e) : 0.f;
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -422,19 +437,19 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
     if (m > 0) fetch_in(m - 1);
 
     // ---- lambda prefix within the 16-position block (DPP), block totals
-    float lin[4][4];
+    float lin[2][4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) lin[ct][j] = row_prefix(lam[ct][j]);
+      for (int j = 0; j < 4; ++j) lin[cl][j] = row_prefix(lam[cl][j]);
     if (li == 15) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        *reinterpret_cast<float4*>(&sBT[J * 64 + 16 * ct + 4 * g]) =
-            make_float4(lin[ct][0], lin[ct][1], lin[ct][2], lin[ct][3]);
+      for (int cl = 0; cl < 2; ++cl)
+        *reinterpret_cast<float4*>(&sBT[J * 64 + 16 * (2 * H + cl) + 4 * g]) =
+            make_float4(lin[cl][0], lin[cl][1], lin[cl][2], lin[cl][3]);
     }
-    // dy_t . v_t and sum_c r u k of the lane's token (over its four lane groups)
-    float bmd = 0.f, dsum = 0.f;
+    // dy_t . v_t of the lane's token (over its four lane groups)
+    float bmd = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const uint32_t vw[4] = {vq[ks].x, vq[ks].y, vq[ks].z, vq[ks].w};
@@ -447,27 +462,14 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
     bmd = rows_sum(bmd);
     lds_barrier();   // B1: block totals visible; the previous chunk's readers are done
 
-    if (!REV) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        float r4[4], k4[4];
-        bf4(cr[ct], r4);
-        bf4(ck[ct], k4);
-        const float4 uu = *reinterpret_cast<const float4*>(&sU[16 * ct + 4 * g]);
-        dsum = fmaf(r4[0] * uu.x, k4[0], dsum);
-        dsum = fmaf(r4[1] * uu.y, k4[1], dsum);
-        dsum = fmaf(r4[2] * uu.z, k4[2], dsum);
-        dsum = fmaf(r4[3] * uu.w, k4[3], dsum);
-      }
-      dsum = rows_sum(dsum);
-    }
-
-    // ---- prefixes; planes kap, S_in, v; G' = 2^Ltot G and <G', S_in> by rows
+    // ---- prefixes; planes kap, q, S_in, G', v, dy; <G', S_in> by rows
     float tot_row = 0.f;   // Ltot of channel 16J + li (the adjoint's rows)
 #pragma unroll
     for (int I = 0; I < 4; ++I) tot_row += sBT[I * 64 + 16 * J + li];
+    float q16[2][4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int cl = 0; cl < 2; ++cl) {
+      const int ct = 2 * H + cl;
       float off[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int I = 0; I < 3; ++I)
@@ -475,66 +477,79 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
           const float4 a = *reinterpret_cast<const float4*>(&sBT[I * 64 + 16 * ct + 4 * g]);
           off[0] += a.x; off[1] += a.y; off[2] += a.z; off[3] += a.w;
         }
-      float k4[4], kap[4];
-      bf4(ck[ct], k4);
+      float r4[4], k4[4], kap[4];
+      bf4(cr[cl], r4);
+      bf4(ck[cl], k4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        lin[ct][j] += off[j];
-        kap[j] = k4[j] * ex2(-lin[ct][j]);
+        lin[cl][j] += off[j];
+        kap[j] = k4[j] * ex2(-lin[cl][j]);
+        q16[cl][j] = r4[j] * ex2(lin[cl][j] - lam[cl][j]);
       }
       wr4<3>(sK, swz(pos, 16 * ct + 4 * g), kap);
+      wr4<3>(sQ, swz(pos, 16 * ct + 4 * g), q16[cl]);
     }
-    float pgs = 0.f;
+    float dsum = 0.f;   // sum_c r u k of the lane's token (the wave's channels)
+    if (!REV) {
+#pragma unroll
+      for (int cl = 0; cl < 2; ++cl) {
+        float r4[4], k4[4];
+        bf4(cr[cl], r4);
+        bf4(ck[cl], k4);
+        const float4 uu = *reinterpret_cast<const float4*>(&sU[16 * (2 * H + cl) + 4 * g]);
+        dsum = fmaf(r4[0] * uu.x, k4[0], dsum);
+        dsum = fmaf(r4[1] * uu.y, k4[1], dsum);
+        dsum = fmaf(r4[2] * uu.z, k4[2], dsum);
+        dsum = fmaf(r4[3] * uu.w, k4[3], dsum);
+      }
+      dsum = rows_sum(dsum);
+      if (g == 0) sPG[128 + 64 * H + pos] = dsum;
+    }
     {
       const float dec = ex2(tot_row);
+      float pgs = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float s4[4] = {ns[nt].x, ns[nt].y, ns[nt].z, ns[nt].w};
+      for (int nl = 0; nl < 2; ++nl) {
+        const int nt = 2 * H + nl;
+        const float s4[4] = {ns[nl].x, ns[nl].y, ns[nl].z, ns[nl].w};
         wr4<3>(sS, swz(16 * J + li, 16 * nt + 4 * g), s4);
+        float g4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          Gc[nt][j] *= dec;
-          pgs = fmaf(Gc[nt][j], s4[j], pgs);
+          Gc[nl][j] *= dec;
+          g4[j] = Gc[nl][j];
+          pgs = fmaf(g4[j], s4[j], pgs);
         }
+        wr4<3>(sG, swz(16 * J + li, 16 * nt + 4 * g), g4);
+      }
+      pgs = rows_sum(pgs);
+      if (g == 0) sPG[64 * H + 16 * J + li] = pgs;
+    }
+    if (m > 0) fetch_s(m - 1);
+    if (H == 0) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        *reinterpret_cast<uint4*>(sV + swz(pos, 32 * ks + 8 * g)) = vq[ks];
+        wr8<3>(sD, swz(pos, 32 * ks + 8 * g), dyf[ks]);
       }
     }
-    pgs = rows_sum(pgs);
-    if (m > 0) fetch_s(m - 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      *reinterpret_cast<uint4*>(sV + swz(pos, 32 * ks + 8 * g)) = vq[ks];
-      wr8<3>(sD, swz(pos, 32 * ks + 8 * g), dyf[ks]);
-    }
-    float q16[4][4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      float r4[4];
-      bf4(cr[ct], r4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) q16[ct][j] = r4[j] * ex2(lin[ct][j] - lam[ct][j]);
-      wr4<3>(sQ, swz(pos, 16 * ct + 4 * g), q16[ct]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const float g4[4] = {Gc[nt][0], Gc[nt][1], Gc[nt][2], Gc[nt][3]};
-      wr4<3>(sG, swz(16 * J + li, 16 * nt + 4 * g), g4);
-    }
     lds_barrier();   // B2: the planes are ready
+    if (!REV) dsum = sPG[128 + pos] + sPG[192 + pos];
 
-    // ---- dr: D rows c (tile ct), column = own position
-    float x16[4][4];
+    // ---- dr: D rows c (tiles 2H, 2H + 1), column = own position
+    float x16[2][4];
     {
-      f32x4 acc[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 bmt[4];   // Bm^T[i][t]: rows i (block I <= J), column t
+      f32x4 acc[2], bmt[4];   // bmt: Bm^T[i][t], rows i (block I <= J), column t
+      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int I = 0; I < 4; ++I) bmt[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const Op<3> dyo = split8<3>(dyf[ks]);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[ct] = mma(rd8<3>(sS, swz(16 * ct + li, 32 * ks + 8 * g)), dyo, acc[ct]);
+        for (int cl = 0; cl < 2; ++cl)
+          acc[cl] = mma(rd8<3>(sS, swz(16 * (2 * H + cl) + li, 32 * ks + 8 * g)), dyo, acc[cl]);
 #pragma unroll
         for (int I = 0; I < 4; ++I)
           if (I <= J) {
@@ -545,35 +560,41 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
       }
       // q_t (S_in dy_t), summed over the wave's positions, for <q^T dY, S_in>
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int cl = 0; cl < 2; ++cl) {
         float zs[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) zs[j] = row_prefix(q16[ct][j] * acc[ct][j]);
-        if (li == 15) *reinterpret_cast<float4*>(&sQS[J * 64 + 16 * ct + 4 * g]) = make_float4(zs[0], zs[1], zs[2], zs[3]);
+        for (int j = 0; j < 4; ++j) zs[j] = row_prefix(q16[cl][j] * acc[cl][j]);
+        if (li == 15)
+          *reinterpret_cast<float4*>(&sQS[J * 64 + 16 * (2 * H + cl) + 4 * g]) = make_float4(zs[0], zs[1], zs[2], zs[3]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (4 * g + j >= li) bmt[J][j] = 0.f;   // keep i < t
+      for (int I = 0; I < 4; ++I)
+        if (I == J) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (4 * g + j >= li) bmt[I][j] = 0.f;   // keep i < t
+        }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb > J) break;
         const Op<3> bo = tiles_op(bmt[2 * kb], bmt[2 * kb + 1]);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[ct] = mma(rdcolpi<3>(sK, kpi[ct], 2048 * kb), bo, acc[ct]);
+        for (int cl = 0; cl < 2; ++cl) acc[cl] = mma(rdcolpi<3>(sK, kpi[cl], 2048 * kb), bo, acc[cl]);
       }
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * H + cl;
         float r4[4], k4[4];
-        bf4(cr[ct], r4);
-        bf4(ck[ct], k4);
+        bf4(cr[cl], r4);
+        bf4(ck[cl], k4);
         const float4 uu = *reinterpret_cast<const float4*>(&sU[16 * ct + 4 * g]);
         const float u4[4] = {uu.x, uu.y, uu.z, uu.w};
         float d[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          d[j] = ex2(lin[ct][j] - lam[ct][j]) * acc[ct][j];
+          d[j] = ex2(lin[cl][j] - lam[cl][j]) * acc[cl][j];
           if (!REV) d[j] = fmaf(u4[j] * k4[j], bmd, d[j]);
-          x16[ct][j] = r4[j] * d[j];
+          x16[cl][j] = r4[j] * d[j];
         }
         out4<REV>(odr, o4 + 64 * ct + 16 * g, d[0], d[1], d[2], d[3]);
       }
@@ -585,7 +606,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) vo[ks].p[0] = __builtin_bit_cast(bf16x8, vq[ks]);
     {
-      f32x4 bm[4];   // Bm[t][i]: rows t (block >= J), column i
+      f32x4 bm[4], acc[2];   // bm: Bm[t][i], rows t (block >= J), column i
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         bm[I] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -595,60 +616,67 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (4 * g + j <= li) bm[J][j] = 0.f;   // keep t > i
-      f32x4 acc[4];
+      for (int I = 0; I < 4; ++I)
+        if (I == J) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < 4; ++j)
+            if (4 * g + j <= li) bm[I][j] = 0.f;   // keep t > i
+        }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acc[ct] = mma(rd8<3>(sG, swz(16 * ct + li, 32 * ks + 8 * g)), vo[ks], acc[ct]);
+      for (int cl = 0; cl < 2; ++cl) {
+        acc[cl] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          acc[cl] = mma(rd8<3>(sG, swz(16 * (2 * H + cl) + li, 32 * ks + 8 * g)), vo[ks], acc[cl]);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb + 1 < J) continue;
         const Op<3> bo = tiles_op(bm[2 * kb], bm[2 * kb + 1]);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[ct] = mma(rdcolpi<3>(sQ, kpi[ct], 2048 * kb), bo, acc[ct]);
+        for (int cl = 0; cl < 2; ++cl) acc[cl] = mma(rdcolpi<3>(sQ, kpi[cl], 2048 * kb), bo, acc[cl]);
       }
-      float xb[4][4], Lj[4][4];
+      float xb[2][4], Lj[2][4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * H + cl;
         float r4[4], k4[4];
-        bf4(cr[ct], r4);
-        bf4(ck[ct], k4);
+        bf4(cr[cl], r4);
+        bf4(ck[cl], k4);
         const float4 uu = *reinterpret_cast<const float4*>(&sU[16 * ct + 4 * g]);
         const float u4[4] = {uu.x, uu.y, uu.z, uu.w};
         float d[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          d[j] = ex2(-lin[ct][j]) * acc[ct][j];
+          d[j] = ex2(-lin[cl][j]) * acc[cl][j];
           if (!REV) d[j] = fmaf(u4[j] * r4[j], bmd, d[j]);
           const float kdk = k4[j] * d[j];
-          const float x = x16[ct][j] - kdk;
+          const float x = x16[cl][j] - kdk;
           const float xi = row_suffix(x);   // this position and the later ones of the block
-          xb[ct][j] = xi;
+          xb[cl][j] = xi;
           // P_j's part from this block, minus k dk, plus r u k (dy . v)
           float L = xi - x - kdk;
           if (!REV) L = fmaf(r4[j] * u4[j] * k4[j], bmd, L);
-          Lj[ct][j] = L;
+          Lj[cl][j] = L;
         }
         out4<REV>(odk, o4 + 64 * ct + 16 * g, d[0], d[1], d[2], d[3]);
       }
       if (li == 0) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          *reinterpret_cast<float4*>(&sXT[J * 64 + 16 * ct + 4 * g]) =
-              make_float4(xb[ct][0], xb[ct][1], xb[ct][2], xb[ct][3]);
+        for (int cl = 0; cl < 2; ++cl)
+          *reinterpret_cast<float4*>(&sXT[J * 64 + 16 * (2 * H + cl) + 4 * g]) =
+              make_float4(xb[cl][0], xb[cl][1], xb[cl][2], xb[cl][3]);
       }
       lds_barrier();   // B5: block sums of x and the q (S dy) sums visible
-      if (g == 0) {   // P at the end of the previous chunk in sweep order
+      if (H == 0 && g == 0) {   // P at the end of the previous chunk in sweep order
         const int c = 16 * J + li;
-        sPend[64 * ((m - 1) & 1) + c] = pgs + sQS[c] + sQS[64 + c] + sQS[128 + c] + sQS[192 + c];
+        sPend[64 * ((m - 1) & 1) + c] =
+            sPG[c] + sPG[64 + c] + sQS[c] + sQS[64 + c] + sQS[128 + c] + sQS[192 + c];
       }
       // dw: P_end + block sums of later waves + the local part, times ln w
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int cl = 0; cl < 2; ++cl) {
+        const int ct = 2 * H + cl;
         float4 pe = *reinterpret_cast<const float4*>(&sPend[64 * (m & 1) + 16 * ct + 4 * g]);
 #pragma unroll
         for (int I = 1; I < 4; ++I)
@@ -657,17 +685,18 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
             pe.x += a.x; pe.y += a.y; pe.z += a.z; pe.w += a.w;
           }
         constexpr float kLn2 = 1.f / kLog2e;
-        out4<REV>(odw, o4 + 64 * ct + 16 * g, (pe.x + Lj[ct][0]) * lam[ct][0] * kLn2,
-                  (pe.y + Lj[ct][1]) * lam[ct][1] * kLn2, (pe.z + Lj[ct][2]) * lam[ct][2] * kLn2,
-                  (pe.w + Lj[ct][3]) * lam[ct][3] * kLn2);
+        out4<REV>(odw, o4 + 64 * ct + 16 * g, (pe.x + Lj[cl][0]) * lam[cl][0] * kLn2,
+                  (pe.y + Lj[cl][1]) * lam[cl][1] * kLn2, (pe.z + Lj[cl][2]) * lam[cl][2] * kLn2,
+                  (pe.w + Lj[cl][3]) * lam[cl][3] * kLn2);
       }
       if (!REV) {
         // u gradient: r k (dy . v) summed over the wave's positions
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int cl = 0; cl < 2; ++cl) {
+          const int ct = 2 * H + cl;
           float r4[4], k4[4];
-          bf4(cr[ct], r4);
-          bf4(ck[ct], k4);
+          bf4(cr[cl], r4);
+          bf4(ck[cl], k4);
           float z[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) z[j] = row_prefix(r4[j] * k4[j] * bmd);
@@ -680,27 +709,19 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
       }
     }
 
-    // ---- dv: D rows n (tile nt), column = own position (key i)
+    // ---- dv: D rows n (tiles 2H, 2H + 1), column = own position (key i)
     {
-      f32x4 acc[4], at[4];   // at: A[t][i], rows t (block >= J), column i
+      f32x4 acc[2], at[4];   // at: A[t][i], rows t (block >= J), column i
+      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        at[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int I = 0; I < 4; ++I) at[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        float x8[8];
+        // the own token's kap over all 64 channels, in pi order, from its plane row
+        const Op<3> ko = rd4x2<3>(sK, swz(pos, 32 * ks + 4 * g), swz(pos, 32 * ks + 16 + 4 * g));
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          float k4[4];
-          bf4(ck[2 * ks + hh], k4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x8[4 * hh + j] = k4[j] * ex2(-lin[2 * ks + hh][j]);
-        }
-        const Op<3> ko = split8<3>(x8);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[nt] = mma(rdcolpi<3>(sG, kpi[nt], 2048 * ks), ko, acc[nt]);
+        for (int nl = 0; nl < 2; ++nl) acc[nl] = mma(rdcolpi<3>(sG, kpi[nl], 2048 * ks), ko, acc[nl]);
 #pragma unroll
         for (int I = 0; I < 4; ++I)
           if (I >= J) {
@@ -709,29 +730,35 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(CbParams p) {
           }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (4 * g + j < li) at[J][j] = 0.f;   // keep t > i
-        if (4 * g + j == li) at[J][j] = REV ? 0.f : dsum;
-      }
+      for (int I = 0; I < 4; ++I)
+        if (I == J) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (4 * g + j < li) at[I][j] = 0.f;   // keep t > i
+            if (4 * g + j == li) at[I][j] = REV ? 0.f : dsum;
+          }
+        }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (2 * kb + 1 < J) continue;
         const Op<3> bo = tiles_op(at[2 * kb], at[2 * kb + 1]);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[nt] = mma(rdcolpi<3>(sD, kpi[nt], 2048 * kb), bo, acc[nt]);
+        for (int nl = 0; nl < 2; ++nl) acc[nl] = mma(rdcolpi<3>(sD, kpi[nl], 2048 * kb), bo, acc[nl]);
       }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) out4<REV>(odv, o4 + 64 * nt + 16 * g, acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
+      for (int nl = 0; nl < 2; ++nl)
+        out4<REV>(odv, o4 + 64 * (2 * H + nl) + 16 * g, acc[nl][0], acc[nl][1], acc[nl][2], acc[nl][3]);
     }
 
-    // ---- adjoint entering the chunk: G <- G' + q^T dY (rows c of wave J)
+    // ---- adjoint entering the chunk: G <- G' + q^T dY (rows c of block J)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const Op<3> qb = rdcol8<3>(sQ, ksg[J], 2048 * ks);
+      const Op<3> qb = rdcol8<3>(sQ, ksj, 2048 * ks);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) Gc[nt] = mma(rdcol8<3>(sD, ksg[nt], 2048 * ks), qb, Gc[nt]);
+      for (int nl = 0; nl < 2; ++nl) Gc[nl] = mma(rdcol8<3>(sD, ksg[nl], 2048 * ks), qb, Gc[nl]);
     }
   }
+
   if (!REV) {
     lds_barrier();   // every wave's u gradient sums are in
     if (tid < 64) p.du_part[(int64_t)b * C + h * HS + tid] = sDU[tid] + sDU[64 + tid] + sDU[128 + tid] + sDU[192 + tid];
@@ -762,10 +789,10 @@ hipError_t enqueue_bwd_chunked(const BwdArgs& a, float* du_part, float* sst, int
   const dim3 grid((unsigned)(a.B * a.H)), block(NT);
   if (rev) {
     hipLaunchKernelGGL(bwd_states_kernel<true>, grid, block, 0, s, p);
-    hipLaunchKernelGGL(bwd_chunk_kernel<true>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(bwd_chunk_kernel<true>, grid, dim3(NTB), 0, s, p);
   } else {
     hipLaunchKernelGGL(bwd_states_kernel<false>, grid, block, 0, s, p);
-    hipLaunchKernelGGL(bwd_chunk_kernel<false>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(bwd_chunk_kernel<false>, grid, dim3(NTB), 0, s, p);
   }
   return hipGetLastError();
 }
