@@ -19,9 +19,11 @@ Prints ONE JSON line (rank 0) with, besides the throughput:
 
 --op selects another entry point of the library on the same workload shapes
 (default wkv6_fwd, the headline):
-  wkv6_bwd   the backward (gradients of sum(y * dy)); token-serial float32
-             vector arithmetic, so its roofline is the fp32 vector peak over
-             the algorithmic flops (12 N^2 per token, head and direction)
+  wkv6_bwd   the backward (gradients of sum(y * dy)): on long bf16 sequences
+             the chunked MFMA kernels, reported against the HBM roofline;
+             otherwise token-serial float32 vector arithmetic, whose roofline
+             is the fp32 vector peak over the algorithmic flops (12 N^2 per
+             token, head and direction)
   wkv6_fwd_gn  the forward with the per-head group normalisation, affine and
              gate fused into its output (bf16 out; y never written)
   wkv6_fwd_then_gn  the same result in the unfused order: wkv6_fwd, then
@@ -57,16 +59,19 @@ MFMA_FLOPS = 2 * 16 * 16 * 32  # one v_mfma_f32_16x16x32_bf16
 METRIC = "WKV6 fwd tokens/s (B·T/s) + % HBM roofline & MFMA util at N=64, 1 GPU"
 
 
+# The sources the forward kernels are compiled from.
+FWD_SOURCES = ("wkv6_device.h", "wkv6_internal.h", "wkv6_kernels.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources (the .hip files and the header they share)
-    with comments and blank lines stripped, so that a recorded counter run
-    stays matched to the kernels it measured; host-only code is left out."""
+    """Hash of the forward kernels' sources (their .hip file and the headers
+    it includes) with comments and blank lines stripped, so that a recorded
+    counter run stays matched to the kernels it measured; host-only code and
+    the other entry points' kernels are left out."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_rnn_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if not name.endswith((".hip", ".h")):
-            continue
+    for name in FWD_SOURCES:
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -132,6 +137,13 @@ def mfma_count(w: I.Workload) -> int:
             if bidir and seg > 0:
                 per_bh += sweep(n, False, False)
     return per_bh * w.B * w.H
+
+
+def bwd_path(w: I.Workload) -> str:
+    """Which kernels the library's backward planner picks for this workload:
+    the chunked MFMA kernels take bf16 calls whose (batch, head) pairs fill
+    the GPU unsegmented (at least 256) over at least 449 tokens."""
+    return "chunked" if w.dtype == "bf16" and w.B * w.H >= 256 and w.T >= 449 else "token-serial"
 
 
 def traffic_record(workload: str):
@@ -335,16 +347,24 @@ def main() -> int:
     mfma_tflops = n_mfma * MFMA_FLOPS / (mean_ms * 1e-3) / 1e12
     traffic = traffic_record(w.name) if op == "wkv6_fwd" else None
     if op == "wkv6_bwd":
-        # algorithmic fp32 vector work: per token, head and direction the state
-        # and adjoint updates (3 N^2 each: a product and a fused multiply-add
-        # per entry) and the dr, dk, dv contractions (2 N^2 each)
+        # algorithmic fp32 work: per token, head and direction the state and
+        # adjoint updates (3 N^2 each: a product and a fused multiply-add per
+        # entry) and the dr, dk, dv contractions (2 N^2 each)
         flops = 12 * w.N * w.N * w.B * w.T * w.H * (2 if w.mode == "bidirectional" else 1)
         tflops = flops / (mean_ms * 1e-3) / 1e12
-        roofline = {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
-                    "kernel": "wkv6_bwd call: token-serial backward sweeps + u reduction",
-                    "mean_call_ms": mean_ms, "algorithmic_flops": flops,
-                    "hbm_achieved_GBps": achieved, "algorithmic_bytes": alg_bytes}
+        if bwd_path(w) == "chunked":
+            # matrix-core kernels: bounded by the HBM bytes
+            roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                        "kernel": "wkv6_bwd call: chunked MFMA kernels (chunk states, gradients) + u reduction",
+                        "mean_call_ms": mean_ms, "algorithmic_bytes": alg_bytes,
+                        "algorithmic_flops": flops, "fp32_tflops": tflops}
+        else:
+            roofline = {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                        "kernel": "wkv6_bwd call: token-serial backward sweeps + u reduction",
+                        "mean_call_ms": mean_ms, "algorithmic_flops": flops,
+                        "hbm_achieved_GBps": achieved, "algorithmic_bytes": alg_bytes}
     else:
         kern = {"wkv6_fwd": "wkv6_fwd call: fast-path sweep kernel + fix-up kernel",
                 "wkv6_fwd_gn": "wkv6_fwd_gn call: fast-path sweep kernel with the fused epilogue + fix-up kernel",
