@@ -1307,7 +1307,11 @@ struct RowSummLds {
 };
 
 
-template <bool BOTH>
+//   WS:   the decay is one bf16 value per channel for every token (RWKV-5):
+//         each lane reads its channel's value once and uses it in place of
+//         the staged w column, so the arithmetic, and the result, are those
+//         of the per-token kernel given that value repeated.
+template <bool BOTH, bool WS>
 __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[RowSummLds::kBytes];
   const int bh = blockIdx.x / p.G, seg = blockIdx.x % p.G;
@@ -1322,7 +1326,8 @@ __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
   const int64_t n = min(T, t_lo + (int64_t)p.SEGC * LC) - t_lo;
   const int nch = (int)((n + LC - 1) / LC);
   const Rsrc rk = slice_rsrc(p.k, base, 2, T, C), rv = slice_rsrc(p.v, base, 2, T, C);
-  const Rsrc rw = slice_rsrc(p.w, base, 2, T, C);
+  const Rsrc rw = slice_rsrc(p.w, WS ? (int64_t)h * HS : base, 2, WS ? 1 : T, C);
+  const float w_ch = WS ? (float)reinterpret_cast<const __bf16*>(p.w)[h * HS + 16 * J + li] : 0.f;
 
   // staging: thread tid moves 16-byte pieces tid and tid + 256 of each tile
   // (row = piece / 8, 8-channel column group = piece % 8)
@@ -1343,7 +1348,7 @@ __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
       const int off = t < n ? (int)(row0 + (uint32_t)t * rstep) + 16 * scol[hh] : kOffNone;
       stg[0][hh] = bload16(rk, off);
       stg[1][hh] = bload16(rv, off);
-      stg[2][hh] = bload16(rw, off);
+      if (!WS) stg[2][hh] = bload16(rw, off);
     }
   };
   int ktJ[2], ktV[4][2];
@@ -1364,7 +1369,7 @@ __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
     char* buf = lds + (ch & 1) * RowSummLds::kBuf;
     // stage this chunk, then send the next chunk's loads out at once
 #pragma unroll
-    for (int ti = 0; ti < 3; ++ti)
+    for (int ti = 0; ti < (WS ? 2 : 3); ++ti)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
         *reinterpret_cast<uint4*>(buf + ti * RowSummLds::kTile + 2 * sdst[hh]) = stg[ti][hh];
@@ -1382,7 +1387,12 @@ __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float w8[8];
-      widen8(rdcol8<1>(sW, ktJ, 2048 * ks).p[0], w8);
+      if constexpr (WS) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w8[j] = w_ch;
+      } else {
+        widen8(rdcol8<1>(sW, ktJ, 2048 * ks).p[0], w8);
+      }
       float run = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1639,8 +1649,8 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   hipError_t e;
   if (pl.G > 1) {
     const dim3 sgrid(bh * pl.G);
-    if constexpr (BF16 && !WS)   // per-token decays from bf16 rows: the row-split summaries
-      hipLaunchKernelGGL((summary_rows_kernel<BIDIR>), sgrid, block, 0, s, p);
+    if constexpr (BF16)   // bf16 rows: the row-split summaries
+      hipLaunchKernelGGL((summary_rows_kernel<BIDIR, WS>), sgrid, block, 0, s, p);
     else if constexpr (BIDIR)
       hipLaunchKernelGGL((summary_both_kernel<BF16, WS>), sgrid, block, 0, s, p);
     else
