@@ -322,15 +322,25 @@ int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H,
  *           batch and the tokens.  T == 0 sets it to zero.
  *
  * B == 0 is a no-op.  The outputs must not overlap one another or any input
- * (INVALID_ARG).  The call runs two token-by-token passes per (batch, head)
- * in float32.  With fewer than 256 (batch, head) pairs it cuts each sequence
- * into up to 63 segments (whole 16-token blocks, at least 64 tokens each):
- * a summary pass then gives each segment its entering state and leaving
- * adjoint, and a last pass completes the decay gradient across segments.
+ * (INVALID_ARG).  Two kernel families compute the same result:
+ *   - bf16 calls with at least 256 (batch, head) pairs and T >= 449 run in
+ *     chunks of 64 tokens on matrix cores: a pass stores every chunk's
+ *     entering state, then a reverse pass with the adjoint in registers
+ *     writes the gradients (operands carried as three bf16 parts, float32
+ *     accumulation; within about 1e-5 of the output's rms).  A (batch, head)
+ *     pair with a 16-token block that decays by 2^-24 or more in some
+ *     channel is recomputed by the other family.
+ *   - every other call runs two token-by-token passes per (batch, head) in
+ *     float32.  With fewer than 256 (batch, head) pairs it cuts each
+ *     sequence into up to 63 segments (whole 16-token blocks, at least 64
+ *     tokens each): a summary pass then gives each segment its entering
+ *     state and leaving adjoint, and a last pass completes the decay
+ *     gradient across segments.
  * Workspace (stream-ordered, from the library's pool as for wkv6_fwd):
  * B*segments*C*4 bytes, plus B*T*C*4 in bidirectional mode, plus
- * B*H*segments*(4*64*64 + 2*64)*4 per direction when segmented.  Errors
- * otherwise as for wkv6_fwd.
+ * B*H*segments*(4*64*64 + 2*64)*4 per direction when segmented, plus, on
+ * the chunked kernels, B*H*ceil(T/64)*64*64*4 bytes of chunk states and
+ * B*H*4 bytes of flags.  Errors otherwise as for wkv6_fwd.
  */
 int wkv6_bwd(int64_t B, int64_t T, int64_t C, int64_t H,
              const void* r, const void* k, const void* v, const void* w_raw,
