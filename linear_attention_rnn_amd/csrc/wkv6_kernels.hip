@@ -906,13 +906,12 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
         for (int nt = 0; nt < 4; ++nt) bstoref4(ry, yoff + 64 * nt, Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
       }
     }
-    if (ch == nch - 1) {
-      if (OUT && !keep_state) {
-        ch = nch;
-        break;
-      }
-    } else {
-      fetch(ch + 1);
+    // unconditional (past the end it reads zeros): with the fetch on one path
+    // only, the compiler's waits where the paths meet covered these loads
+    fetch(ch + 1);
+    if (ch == nch - 1 && OUT && !keep_state) {
+      ch = nch;
+      break;
     }
 
     // ---- phase D: state rows 16J + 4g + j (registers only; sS is written
