@@ -141,9 +141,11 @@ def mfma_count(w: I.Workload) -> int:
 
 def bwd_path(w: I.Workload) -> str:
     """Which kernels the library's backward planner picks for this workload:
-    the chunked MFMA kernels take bf16 calls whose (batch, head) pairs fill
-    the GPU unsegmented (at least 256) over at least 449 tokens."""
-    return "chunked" if w.dtype == "bf16" and w.B * w.H >= 256 and w.T >= 449 else "token-serial"
+    the chunked MFMA kernels take bf16 calls of at least 64 tokens that run
+    unsegmented (at least 256 (batch, head) pairs, or fewer than 128
+    tokens)."""
+    unsegmented = w.B * w.H >= 256 or w.T < 128
+    return "chunked" if w.dtype == "bf16" and w.T >= 64 and unsegmented else "token-serial"
 
 
 def traffic_record(workload: str):

@@ -323,8 +323,8 @@ int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H,
  *
  * B == 0 is a no-op.  The outputs must not overlap one another or any input
  * (INVALID_ARG).  Two kernel families compute the same result:
- *   - bf16 calls with at least 256 (batch, head) pairs and T >= 449 run in
- *     chunks of 64 tokens on matrix cores: a pass stores every chunk's
+ *   - bf16 calls with T >= 64 that run unsegmented (at least 256 (batch,
+ *     head) pairs, or T < 128) run in chunks of 64 tokens on matrix cores: a pass stores every chunk's
  *     entering state, then a reverse pass with the adjoint in registers
  *     writes the gradients (operands carried as three bf16 parts, float32
  *     accumulation; within about 1e-5 of the output's rms).  A (batch, head)

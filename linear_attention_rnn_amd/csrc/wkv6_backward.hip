@@ -821,12 +821,13 @@ struct BwdWs {
 };
 
 // The chunked kernels take bf16 calls whose items run unsegmented, over at
-// least kChunkedMinT tokens: they run one workgroup per CU, so on short
-// sequences with many items (B64 T196 H12: 491 against 444 us) the
-// token-serial kernels, three workgroups per CU, are faster; over long ones
-// the chunked kernels are (B8 T4096 H32: 1.09 against 1.80 ms).
+// least one whole chunk: they work in 64-token chunks, so on shorter
+// sequences the token-serial kernels are faster (B64 T33 H12 bidirectional:
+// 101 against 114 us); from one chunk on the chunked kernels are (same box:
+// T64 134 against 139 us, T196 382 against 391 us, T320 507 against 622 us;
+// B8 T1000 H32 causal 241 against 479 us).
 // WKV6_BWD_CHUNKED=1 / 0 forces the choice for such calls.
-constexpr int64_t kChunkedMinT = 449;
+constexpr int64_t kChunkedMinT = 64;
 
 bool use_chunked(const BwdArgs& a, const BwdPlan& pl) {
   if (!a.bf16 || pl.G != 1) return false;
