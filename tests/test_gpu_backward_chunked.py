@@ -78,3 +78,19 @@ def test_chunked_long_text_rows(torch_cuda):
     w = I.workload("text-long-causal-bf16")
     x = I.random_inputs(2, w.T, w.C, w.H, seed=w.seed, dtype="bf16", wraw_lo=-8.0, wraw_hi=-1.0)
     check("chunked text-long rows (B=2)", x, dy_of(x, w.seed + 1000), w.H, "causal", "bf16")
+
+
+def test_chunked_item_slow_in_reverse_only(torch_cuda):
+    """An item whose fast decays fill one 16-token block of the reversed
+    sweep but straddle two blocks of the forward one (T = 150 is not a
+    multiple of 16, so the blocks of the two directions differ): only the
+    reverse direction flags it, after the forward direction's chunked kernel
+    has already written its gradients; the token-serial kernels then
+    recompute the whole item.  Here tokens 118..133 (reversed-sweep block
+    [118, 134)) decay by 2^-1.7 each in one channel: 2^-27.2 in that block,
+    2^-17 and 2^-10.2 in the forward blocks [112, 128) and [128, 144)."""
+    B, T, H = 2, 150, 2
+    x = I.random_inputs(B, T, 64 * H, H, seed=1970, dtype="bf16", wraw_lo=-8.0, wraw_hi=-2.0)
+    w_fast = float(np.log(1.7 / np.log2(np.e)))
+    x["w_raw"][1, 118:134, 64 + 7] = I.round_to_bf16(np.float32(w_fast))
+    check("chunked slow in the reverse direction only", x, dy_of(x, 1971), H, "bidirectional", "bf16")
