@@ -879,12 +879,15 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) a = mma(rd8<SP>(sK, 1024 * I + lo.a[ks]), q[ks], a);
           }
-          // key i < tau keeps its score (every key of an earlier block
-          // does; a is zero for a later block), i == tau takes the bonus
+          // every key of an earlier block keeps its score (a is zero for a
+          // later block); in the query's own block only the keys before it
+          // do, and its own key takes the bonus.  The lane masks depend on
+          // j alone, so four of each serve every block.
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int i = 16 * I + 4 * g + j;
-            mx[4 * hh + j] = i < tau ? a[j] : ((DIAG && i == tau) ? dg : 0.f);
+            const int d = 4 * g + j - li;   // key minus query inside the block
+            const float own = d < 0 ? a[j] : ((DIAG && d == 0) ? dg : 0.f);
+            mx[4 * hh + j] = I == J ? own : a[j];
           }
         }
         const Op<SP> mo = split8<SP>(mx);
