@@ -339,8 +339,8 @@ int wkv6_fwd_state(int64_t B, int64_t T, int64_t C, int64_t H,
  * Workspace (stream-ordered, from the library's pool as for wkv6_fwd):
  * B*segments*C*4 bytes, plus B*T*C*4 in bidirectional mode, plus
  * B*H*segments*(4*64*64 + 2*64)*4 per direction when segmented, plus, on
- * the chunked kernels, B*H*ceil(T/64)*64*64*4 bytes of chunk states and
- * B*H*4 bytes of flags.  Errors otherwise as for wkv6_fwd.
+ * the chunked kernels, B*H*ceil(T/64)*64*64*4 bytes of chunk states per
+ * direction and B*H*4 bytes of flags.  Errors otherwise as for wkv6_fwd.
  */
 int wkv6_bwd(int64_t B, int64_t T, int64_t C, int64_t H,
              const void* r, const void* k, const void* v, const void* w_raw,

@@ -817,7 +817,7 @@ BwdPlan bwd_plan(const BwdArgs& a) {
 }
 
 struct BwdWs {
-  size_t du, drtmp, dir[2], sst, slow, total;   // byte offsets; dir: carries of each direction
+  size_t du, drtmp, dir[2], sst[2], slow, total;   // byte offsets; dir: carries, sst: chunk states of each direction
 };
 
 // The chunked kernels take bf16 calls whose items run unsegmented, over at
@@ -849,10 +849,13 @@ BwdWs bwd_ws(const BwdArgs& a, const BwdPlan& pl) {
     w.dir[d] = n;
     if (d == 0 || a.bidirectional) n += up256(per);
   }
-  w.sst = w.slow = n;
+  w.sst[0] = w.sst[1] = w.slow = n;
   if (use_chunked(a, pl)) {
     const size_t nch = (size_t)((a.T + 63) / 64);
-    n += up256((size_t)a.B * a.H * nch * NT * 16 * 4);
+    for (int d = 0; d < (a.bidirectional ? 2 : 1); ++d) {
+      w.sst[d] = n;
+      n += up256((size_t)a.B * a.H * nch * NT * 16 * 4);
+    }
     w.slow = n;
     n += up256((size_t)a.B * a.H * 4);
   }
@@ -927,10 +930,19 @@ hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t s) {
   hipError_t e;
   if (use_chunked(a, pl)) {
     // chunked kernels, then the token-serial ones for the items they flagged
+    // both directions' chunk states first (so that either direction's flag
+    // skips an item in both gradient passes), then the two gradient passes
+    // back to back: the reversed one adds to outputs the forward one has
+    // just written
     int* slow = reinterpret_cast<int*>(ws + lay.slow);
-    float* sst = reinterpret_cast<float*>(ws + lay.sst);
-    for (int d = 0; d < (a.bidirectional ? 2 : 1); ++d)
-      if ((e = enqueue_bwd_chunked(a, p.du_part, sst, slow, d == 1, s)) != hipSuccess) return e;
+    const int nd = a.bidirectional ? 2 : 1;
+    for (int d = 0; d < nd; ++d)
+      if ((e = enqueue_bwd_chunk_states(a, reinterpret_cast<float*>(ws + lay.sst[d]), slow, d == 1, s)) != hipSuccess)
+        return e;
+    for (int d = 0; d < nd; ++d)
+      if ((e = enqueue_bwd_chunk_grads(a, p.du_part, reinterpret_cast<const float*>(ws + lay.sst[d]), slow, d == 1,
+                                       s)) != hipSuccess)
+        return e;
     p.only = slow;
     for (int d = 0; d < (a.bidirectional ? 2 : 1); ++d) {
       launch_bwd(a.bf16, d == 1, false, grid, s, p);

@@ -319,7 +319,10 @@ constexpr int NTB = 512;
 template <bool REV>
 __global__ __launch_bounds__(NTB, 1) void bwd_chunk_kernel(CbParams p) {
   __shared__ __attribute__((aligned(16))) char lds[CbLds::kBytes];
-  const int bh = blockIdx.x;
+  // the reversed sweep visits the items in reverse order: it runs right
+  // after the forward direction's pass, whose last outputs, which it adds
+  // to first, are then the likeliest still to be in the caches
+  const int bh = REV ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
   if (p.slow[bh]) return;   // the token-serial kernels take this item
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -765,9 +768,7 @@ __global__ __launch_bounds__(NTB, 1) void bwd_chunk_kernel(CbParams p) {
   }
 }
 
-}  // namespace
-
-hipError_t enqueue_bwd_chunked(const BwdArgs& a, float* du_part, float* sst, int* slow, bool rev, hipStream_t s) {
+CbParams chunk_params(const BwdArgs& a, float* du_part, const float* sst, const int* slow) {
   CbParams p{};
   p.r = a.r;
   p.k = a.k;
@@ -780,20 +781,35 @@ hipError_t enqueue_bwd_chunked(const BwdArgs& a, float* du_part, float* sst, int
   p.dv = a.dv;
   p.dw = a.dw_raw;
   p.du_part = du_part;
-  p.sst = sst;
-  p.slow = slow;
+  p.sst = const_cast<float*>(sst);
+  p.slow = const_cast<int*>(slow);
   p.T = a.T;
   p.C = a.C;
   p.H = (int)a.H;
   p.nch = (int)((a.T + LC - 1) / LC);
-  const dim3 grid((unsigned)(a.B * a.H)), block(NT);
-  if (rev) {
-    hipLaunchKernelGGL(bwd_states_kernel<true>, grid, block, 0, s, p);
+  return p;
+}
+
+}  // namespace
+
+hipError_t enqueue_bwd_chunk_states(const BwdArgs& a, float* sst, int* slow, bool rev, hipStream_t s) {
+  const CbParams p = chunk_params(a, nullptr, sst, slow);
+  const dim3 grid((unsigned)(a.B * a.H));
+  if (rev)
+    hipLaunchKernelGGL(bwd_states_kernel<true>, grid, dim3(NT), 0, s, p);
+  else
+    hipLaunchKernelGGL(bwd_states_kernel<false>, grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t enqueue_bwd_chunk_grads(const BwdArgs& a, float* du_part, const float* sst, const int* slow, bool rev,
+                                   hipStream_t s) {
+  const CbParams p = chunk_params(a, du_part, sst, slow);
+  const dim3 grid((unsigned)(a.B * a.H));
+  if (rev)
     hipLaunchKernelGGL(bwd_chunk_kernel<true>, grid, dim3(NTB), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(bwd_states_kernel<false>, grid, block, 0, s, p);
+  else
     hipLaunchKernelGGL(bwd_chunk_kernel<false>, grid, dim3(NTB), 0, s, p);
-  }
   return hipGetLastError();
 }
 

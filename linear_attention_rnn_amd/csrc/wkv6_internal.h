@@ -75,13 +75,16 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(const BwdArgs& a);
 hipError_t enqueue_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
 
-// One direction of the chunked backward on MFMA (bf16 inputs, one workgroup
-// per (batch, head); wkv6_backward_chunked.hip): the chunk-entry states into
-// sst ([B*H][ceil(T/64)][256][16] floats), then the gradients; items that
-// need the general decay path are flagged in slow ([B*H]) and skipped.
-// rev: the reversed sweep of a bidirectional call (adds to the outputs).
-hipError_t enqueue_bwd_chunked(const BwdArgs& a, float* du_part, float* sst, int* slow, bool rev,
-                               hipStream_t stream);
+// The chunked backward on MFMA (bf16 inputs, one workgroup per (batch,
+// head); wkv6_backward_chunked.hip), one direction per call.  States: the
+// chunk-entry states into sst ([B*H][ceil(T/64)][256][16] floats); items
+// that need the general decay path are flagged in slow ([B*H]; the forward
+// direction sets every flag, the reversed one only adds flags).  Gradients:
+// from those states, skipping flagged items.  rev: the reversed sweep of a
+// bidirectional call (adds to the outputs).
+hipError_t enqueue_bwd_chunk_states(const BwdArgs& a, float* sst, int* slow, bool rev, hipStream_t stream);
+hipError_t enqueue_bwd_chunk_grads(const BwdArgs& a, float* du_part, const float* sst, const int* slow, bool rev,
+                                   hipStream_t stream);
 
 // Per-head group normalisation, affine and gate of a y in memory
 // (wkv6_groupnorm.hip): out = ((y - mean) * rstd * gamma + beta) * g, bf16.
