@@ -1346,8 +1346,8 @@ __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
   auto fetch = [&](int ch) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int t = ch * LC + srow[hh];   // rows past the segment read zero
-      const int off = t < n ? (int)(row0 + (uint32_t)t * rstep) + 16 * scol[hh] : kOffNone;
+      const int t = ch * LC + srow[hh];   // rows outside the segment read zero
+      const int off = t >= 0 && t < n ? (int)(row0 + (uint32_t)t * rstep) + 16 * scol[hh] : kOffNone;
       stg[0][hh] = bload16(rk, off);
       stg[1][hh] = bload16(rv, off);
       if (!WS) stg[2][hh] = bload16(rw, off);
@@ -1364,18 +1364,22 @@ __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
     S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     R[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float P = 0.f;   // the segment's log2 decay before the chunk, channel 16J + li
+  // BOTH: the segment's log2 decay before the chunk; else the decay after it
+  // (the forward summary runs the chunks last to first), channel 16J + li
+  float P = 0.f;
   const bool odd = (g & 1) != 0, upper = (g & 2) != 0;
 
-  auto step = [&](int ch) {
-    char* buf = lds + (ch & 1) * RowSummLds::kBuf;
+  // chunk ch staged into buffer i (the two alternate); nx: the chunk to fetch
+  // next (past either end it reads zeros)
+  auto step = [&](int ch, int i, int nx) {
+    char* buf = lds + i * RowSummLds::kBuf;
     // stage this chunk, then send the next chunk's loads out at once
 #pragma unroll
     for (int ti = 0; ti < (WS ? 2 : 3); ++ti)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
         *reinterpret_cast<uint4*>(buf + ti * RowSummLds::kTile + 2 * sdst[hh]) = stg[ti][hh];
-    if (ch + 1 < nch) fetch(ch + 1);
+    fetch(nx);
     lds_barrier();   // (the other buffer's readers finished before the previous barrier)
     const __bf16* sK = reinterpret_cast<const __bf16*>(buf);
     const __bf16* sV = reinterpret_cast<const __bf16*>(buf + RowSummLds::kTile);
@@ -1420,14 +1424,18 @@ __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
       tot += pair + other;
     }
 
-    // S <- 2^tot S + (k 2^(tot - Lin))^T V;  R <- R + (k 2^(P + Lex))^T V.
-    // The accumulator entries of a lane all belong to its channel, so the
-    // decay is one factor per lane.
-    const float dec = ex2(tot);
+    // BOTH: S <- 2^tot S + (k 2^(tot - Lin))^T V;  R <- R + (k 2^(P + Lex))^T V.
+    // Else, the chunks last to first: S <- S + (k 2^(P + tot - Lin))^T V,
+    // every part decayed once to the segment's end.  The accumulator entries
+    // of a lane all belong to its channel, so a decay is one factor per lane.
+    if constexpr (BOTH) {
+      const float dec = ex2(tot);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[nt][j] *= dec;
+        for (int j = 0; j < 4; ++j) S[nt][j] *= dec;
+    }
+    const float post = BOTH ? tot : P + tot;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if (32 * ks >= Lv) break;
@@ -1435,7 +1443,7 @@ __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
       widen8(rdcol8<1>(sK, ktJ, 2048 * ks).p[0], k8);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        ef[j] = k8[j] * ex2(tot - lin[ks][j]);
+        ef[j] = k8[j] * ex2(post - lin[ks][j]);
         if (BOTH) er[j] = k8[j] * ex2(P + lex[ks][j]);
       }
       const Op<2> eo = split8<2>(ef);
@@ -1450,8 +1458,16 @@ __global__ __launch_bounds__(NT, 3) void summary_rows_kernel(Params p) {
     }
     P += tot;
   };
-  fetch(0);
-  for (int ch = 0; ch < nch; ++ch) step(ch);
+  // The forward-only summary runs its chunks last to first: the ones it
+  // reads last, a segment's first, are then the likeliest still to be in
+  // the caches when the sweeps start there.
+  if constexpr (BOTH) {
+    fetch(0);
+    for (int ch = 0; ch < nch; ++ch) step(ch, ch & 1, ch + 1);
+  } else {
+    fetch(nch - 1);
+    for (int ch = nch - 1; ch >= 0; --ch) step(ch, ch & 1, ch - 1);
+  }
 
   // S^T[n][c] (and R^T) with n = 16 nt + 4g + j, c = 16J + li; the segment's
   // total log2 decay of channel 16J + li from the lanes of row 0
