@@ -217,8 +217,9 @@ __device__ __forceinline__ Rsrc slice_rsrc(const void* p, int64_t elem_off, int 
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, nbytes, kRsrcFlags);
 }
 
+template <int AUX = 0>
 __device__ __forceinline__ uint4 bload16(Rsrc r, int off) {
-  const auto q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  const auto q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
   return make_uint4(q[0], q[1], q[2], q[3]);
 }
 
@@ -227,10 +228,14 @@ __device__ __forceinline__ float4 bloadf4(Rsrc r, int off) {
   return make_float4(__uint_as_float(q[0]), __uint_as_float(q[1]), __uint_as_float(q[2]), __uint_as_float(q[3]));
 }
 
+// AUX: the cache policy bits of the access (kStream: the non-temporal hint,
+// for data not read again soon)
+constexpr int kStream = 2;
+template <int AUX = 0>
 __device__ __forceinline__ void bstoref4(Rsrc r, int off, float a, float b, float c, float d) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 q = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
-  __builtin_amdgcn_raw_buffer_store_b128(q, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(q, r, off, 0, AUX);
 }
 
 // Sum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48):

@@ -248,17 +248,17 @@ __device__ __forceinline__ void gn_gate_store(f32x4 (&Y)[4], const GateRaw<BF16>
 }
 
 // The lane's row: row_off is the row's byte offset in the slice.
-template <bool BF16>
+template <bool BF16, int AUX = 0>
 __device__ __forceinline__ Raw<BF16> gload(Rsrc rs, int row_off, int g) {
   Raw<BF16> r;
   if constexpr (BF16) {
-    r.q[0] = bload16(rs, row_off + 16 * g);
-    r.q[1] = bload16(rs, row_off + 64 + 16 * g);
+    r.q[0] = bload16<AUX>(rs, row_off + 16 * g);
+    r.q[1] = bload16<AUX>(rs, row_off + 64 + 16 * g);
   } else {
-    r.q[0] = bload16(rs, row_off + 32 * g);
-    r.q[1] = bload16(rs, row_off + 32 * g + 16);
-    r.q[2] = bload16(rs, row_off + 128 + 32 * g);
-    r.q[3] = bload16(rs, row_off + 128 + 32 * g + 16);
+    r.q[0] = bload16<AUX>(rs, row_off + 32 * g);
+    r.q[1] = bload16<AUX>(rs, row_off + 32 * g + 16);
+    r.q[2] = bload16<AUX>(rs, row_off + 128 + 32 * g);
+    r.q[3] = bload16<AUX>(rs, row_off + 128 + 32 * g + 16);
   }
   return r;
 }
@@ -779,7 +779,7 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     // tokens past the segment read zero
     const bool in_seg = tau < (int)min<int64_t>(LC, n - (int64_t)ch * LC);
     const int off = at(in_seg, in_row0, in_step, ch);
-    if (OUT) buf[0] = gload<BF16>(rr, off, g);
+    if (OUT) buf[0] = gload<BF16, CAUSAL_OUT ? kStream : 0>(rr, off, g);
     buf[1] = gload<BF16>(rk, off, g);
     buf[2] = gload<BF16>(rv, off, g);
     buf[3] = gload<BF16>(rw, WS ? (in_seg ? 0 : kOffNone) : off, g);
@@ -906,7 +906,8 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
         gn_gate_store<BF16>(Y, gt, sGm, sGm + 64, g, p.eps, ro, at(valid, o_row0, o_step, ch));
       } else {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) bstoref4(ry, yoff + 64 * nt, Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
+        for (int nt = 0; nt < 4; ++nt)
+          bstoref4<CAUSAL_OUT ? kStream : 0>(ry, yoff + 64 * nt, Y[nt][0], Y[nt][1], Y[nt][2], Y[nt][3]);
       }
     }
     // unconditional (past the end it reads zeros): with the fetch on one path
