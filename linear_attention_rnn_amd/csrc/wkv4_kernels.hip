@@ -117,7 +117,7 @@ __device__ __forceinline__ void run(const P4& p, St& s, int b, int64_t c, int64_
     for (int j = 0; j < U4; ++j) {
       if (t0 + j < t_hi) {
         const float y = step<OUT>(s, kc[j], vc[j], wl, ul);
-        if (OUT) p.y[base + (t0 + j) * p.C] = y;
+        if (OUT) __builtin_nontemporal_store(y, &p.y[base + (t0 + j) * p.C]);   // not read again
       }
     }
 #pragma unroll
