@@ -128,6 +128,49 @@ __device__ __forceinline__ void run(const P4& p, St& s, int b, int64_t c, int64_
   }
 }
 
+// The summary of tokens [t_lo, t_hi) taken from the last token to the first:
+// token t weighs 2^(k_t log2 e - (t_hi - 1 - t) w log2 e), so with d the
+// decay since the segment's end the same running-maximum form accumulates
+// (a, b, p) with every factor at most 1.  The tokens it reads last, the
+// segment's first, are then the likeliest still to be in the caches when
+// the output kernel starts there.
+template <bool BF16>
+__device__ __forceinline__ void summary_backwards(const P4& p, St& s, int b, int64_t c, int64_t t_lo,
+                                                  int64_t t_hi, float wl) {
+  const int64_t base = (int64_t)b * p.T * p.C + c;
+  float kc[U4], vc[U4], kn[U4], vn[U4];
+  auto load = [&](int64_t t0, float (&kk)[U4], float (&vv)[U4]) {   // tokens t0, t0 - 1, ..
+#pragma unroll
+    for (int j = 0; j < U4; ++j) {
+      const int64_t t = t0 - j >= t_lo ? t0 - j : t_lo;   // past the start: repeat the first token (unused)
+      kk[j] = ld<BF16>(p.k, base + t * p.C);
+      vv[j] = ld<BF16>(p.v, base + t * p.C);
+    }
+  };
+  float d = 0.f;
+  load(t_hi - 1, kc, vc);
+  for (int64_t t0 = t_hi - 1; t0 >= t_lo; t0 -= U4) {
+    load(t0 - U4 >= t_lo ? t0 - U4 : t0, kn, vn);   // the next group is in flight during this one
+#pragma unroll
+    for (int j = 0; j < U4; ++j) {
+      if (t0 - j >= t_lo) {
+        const float e = kc[j] * kL2e - d;
+        float f1, f2;   // 2^(p - p'), 2^(e - p') with p' = max(p, e)
+        pair_scale(s.p, e, f1, f2);
+        s.a = fmaf(f1, s.a, f2 * vc[j]);
+        s.b = fmaf(f1, s.b, f2);
+        s.p = fmaxf(s.p, e);
+        d += wl;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U4; ++j) {
+      kc[j] = kn[j];
+      vc[j] = vn[j];
+    }
+  }
+}
+
 __device__ __forceinline__ bool item(const P4& p, int& b, int& g, int64_t& c) {
   c = (int64_t)blockIdx.y * NT4 + threadIdx.x;
   b = blockIdx.x / p.G;
@@ -142,7 +185,7 @@ __global__ __launch_bounds__(NT4) void wkv4_summary_kernel(P4 p) {
   if (!item(p, b, g, c)) return;
   const int64_t t_lo = g * p.SEGL, t_hi = min(p.T, t_lo + p.SEGL);
   St s{0.f, 0.f, -INFINITY};
-  run<BF16, false>(p, s, b, c, t_lo, t_hi, p.w[c] * kL2e, 0.f);
+  summary_backwards<BF16>(p, s, b, c, t_lo, t_hi, p.w[c] * kL2e);
   float* o = p.summ + ((int64_t)b * p.G + g) * 3 * p.C + c;
   o[0] = s.a;
   o[p.C] = s.b;
