@@ -713,21 +713,37 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
     have_S = true;
   }
   if (CARRY) {
-    // (g1, S1) o (g2, S2) = (g1 + g2, 2^g2 S1 + S2) over the earlier segments
+    // (g1, S1) o (g2, S2) = (g1 + g2, 2^g2 S1 + S2) over the earlier segments,
+    // in sweep order.  The summaries are loaded kGrp at a time, every load of
+    // a group issued before the first combine, so a group costs one memory
+    // latency rather than kGrp.  Slots past the last summary re-read the last
+    // one (addresses stay valid, loads stay unconditional) and are skipped.
+    constexpr int kGrp = 4;
     const int nprev = REV ? p.G - 1 - seg : seg;
-    for (int k2 = 0; k2 < nprev; ++k2) {
-      const int s2 = REV ? p.G - 1 - k2 : k2;
-      const float* Ss = p.summ + (((int64_t)bh * p.G + s2) * 2 + (REV ? 1 : 0)) * kSummFloats;
-      float gj[4];
+    for (int k0 = 0; k0 < nprev; k0 += kGrp) {
+      const int cnt = min(kGrp, nprev - k0);
+      float4 gl[kGrp], f[kGrp][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) gj[j] = ex2(Ss[PL + 16 * J + 4 * g + j]);
+      for (int u = 0; u < kGrp; ++u) {
+        const int k2 = k0 + min(u, cnt - 1);
+        const int s2 = REV ? p.G - 1 - k2 : k2;
+        const float* Ss = p.summ + (((int64_t)bh * p.G + s2) * 2 + (REV ? 1 : 0)) * kSummFloats;
+        gl[u] = *reinterpret_cast<const float4*>(Ss + PL + 16 * J + 4 * g);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float4 f = *reinterpret_cast<const float4*>(Ss + (16 * nt + li) * HS + 16 * J + 4 * g);
-        S[nt][0] = S[nt][0] * gj[0] + f.x;
-        S[nt][1] = S[nt][1] * gj[1] + f.y;
-        S[nt][2] = S[nt][2] * gj[2] + f.z;
-        S[nt][3] = S[nt][3] * gj[3] + f.w;
+        for (int nt = 0; nt < 4; ++nt)
+          f[u][nt] = *reinterpret_cast<const float4*>(Ss + (16 * nt + li) * HS + 16 * J + 4 * g);
+      }
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) {
+        if (u >= cnt) break;   // uniform
+        const float gj[4] = {ex2(gl[u].x), ex2(gl[u].y), ex2(gl[u].z), ex2(gl[u].w)};
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          S[nt][0] = S[nt][0] * gj[0] + f[u][nt].x;
+          S[nt][1] = S[nt][1] * gj[1] + f[u][nt].y;
+          S[nt][2] = S[nt][2] * gj[2] + f[u][nt].z;
+          S[nt][3] = S[nt][3] * gj[3] + f[u][nt].w;
+        }
       }
     }
     have_S = have_S || nprev > 0;

@@ -88,6 +88,28 @@ def test_decay_extremes(torch_cuda, case, mode):
     assert e <= TOL["f32"]
 
 
+@pytest.mark.parametrize("B,H", [(64, 12), (40, 64)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["causal", "bidirectional"])
+def test_many_slow_items(torch_cuda, B, H, mode, dtype):
+    """Every third (batch, head) item decays fast enough (w_raw = 1.5) that its
+    chunks need the general sweeps, among 768 and 2560 items: the fix-up
+    launch recomputes exactly the marked items and leaves the others'
+    outputs as the fast kernel wrote them."""
+    T = 70
+    C = 64 * H
+    x = I.random_inputs(B, T, C, H, seed=91, dtype=dtype)
+    item = np.arange(B)[:, None] * H + np.arange(H)[None, :]
+    slow = (item % 3 == 1)                      # [B, H]
+    mask = np.repeat(slow, 64, axis=1)[:, None, :]   # [B, 1, C]
+    x["w_raw"] = np.where(mask, np.float32(1.5), x["w_raw"]).astype(np.float32)
+    y = gpu_fwd(x, H, mode, dtype)
+    y_ref = wkv6_ref(x["r"], x["k"], x["v"], x["w_raw"], x["u"], H, mode)
+    e = err_over_rms(y, y_ref)
+    say(f"[slow items] B={B} H={H} {mode} {dtype}: {e:.3e}")
+    assert e <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_reversal_invariant_on_gpu(torch_cuda, dtype):
     """Reversing the sequence reverses the bidirectional output."""
