@@ -192,6 +192,116 @@ __global__ __launch_bounds__(NT4) void wkv4_summary_kernel(P4 p) {
   o[2 * p.C] = s.p;
 }
 
+// The same summaries for bf16 inputs with C a multiple of 8, their k and v
+// rows staged through LDS by direct-to-LDS loads (global_load_lds_dwordx4):
+// the bytes in flight then need no registers, so a workgroup keeps three
+// groups of kRowsL tokens of k and v in flight (24 KB) while it reads a
+// fourth, where the register-staged kernel keeps 8 KB.  Each thread loads one 16-byte
+// piece (8 channels of one token) of each array per group; a group's tile
+// is kRowsL rows of the workgroup's 256 channels.  Pieces past the last
+// channel (wholly, since C % 8 == 0) re-read the block's first piece, and
+// rows before the segment re-read its first token; neither is used.
+constexpr int kRowsL = 8;     // tokens per staged group
+constexpr int kSlotsL = 4;    // groups resident in LDS
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ void lds_barrier4() {   // waits for LDS operations only
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(NT4) void wkv4_summary_lds_kernel(P4 p) {
+  __shared__ __attribute__((aligned(16))) char tiles[kSlotsL][2][kRowsL * NT4 * 2];
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t c0 = (int64_t)blockIdx.y * NT4, c = c0 + tid;
+  const int b = blockIdx.x / p.G, g = blockIdx.x % p.G;
+  const int64_t t_lo = g * p.SEGL, t_hi = min(p.T, t_lo + p.SEGL);
+  const int ngr = (int)((t_hi - t_lo + kRowsL - 1) / kRowsL);
+  // this thread's piece of a group tile: row tid / 32, channels 8 (tid % 32)..
+  const int prow = tid >> 5;
+  const int64_t pch = c0 + 8 * (tid & 31);
+  const int64_t rowb = p.C * 2;   // bytes per token row
+  const int64_t off0 = ((int64_t)b * p.T * p.C + (pch < p.C ? pch : c0)) * 2;
+  const char* kb = static_cast<const char*>(p.k) + off0;
+  const char* vb = static_cast<const char*>(p.v) + off0;
+  // group gi: tokens t_hi - 1 - (gi kRowsL + r), r = 0.., the segment's last first
+  auto issue = [&](int gi) {
+    int64_t t = t_hi - 1 - ((int64_t)gi * kRowsL + prow);
+    if (t < t_lo) t = t_lo;
+    char* tk = tiles[gi % kSlotsL][0] + wv * 1024;   // lane l's 16 bytes land at + 16 l
+    char* tv = tiles[gi % kSlotsL][1] + wv * 1024;
+    __builtin_amdgcn_global_load_lds(kb + t * rowb, (lds_void*)tk, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + t * rowb, (lds_void*)tv, 16, 0, 0);
+  };
+  // The channel's decay goes to LDS the same way, ahead of group 0 (so it has
+  // landed when group 0 has); the first groups are issued unconditionally
+  // (past a short segment's end they re-read its first token).
+  __shared__ __attribute__((aligned(16))) float wsh[NT4];
+  __builtin_amdgcn_global_load_lds(p.w + (c < p.C ? c : c0), (lds_void*)(wsh + 64 * wv), 4, 0, 0);
+#pragma unroll
+  for (int gi = 0; gi < kSlotsL - 1; ++gi) issue(gi);
+  St s{0.f, 0.f, -INFINITY};
+  float d = 0.f;
+  for (int gi = 0; gi < ngr; ++gi) {
+    // this wave's two loads of group gi are done once at most those of the
+    // groups issued after it remain (loads complete in order; near the end,
+    // where fewer were issued after it than the count allows for, the wait
+    // is only longer than needed)
+    const int later = min(ngr - 1 - gi, kSlotsL - 2);
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // every wave's loads of group gi have landed, and every wave has read
+    // group gi - 1, whose slot the next issue reuses
+    lds_barrier4();
+    if (gi + kSlotsL - 1 < ngr) issue(gi + kSlotsL - 1);
+    // The group's rows (and the decay) are read in one asm block that waits
+    // for its own LDS reads: written as plain reads, they would get a wait
+    // for every direct-to-LDS load in flight (the compiler cannot tell the
+    // slots apart), the ones just issued included.
+    const uint32_t la = (uint32_t)(uintptr_t)(lds_char*)(tiles[gi % kSlotsL][0]) + 2u * (uint32_t)tid;
+    const uint32_t lw = (uint32_t)(uintptr_t)(lds_char*)(wsh) + 4u * (uint32_t)tid;
+    uint32_t kr[kRowsL], vr[kRowsL], wbits;
+    asm volatile(
+        "ds_read_u16 %0, %17\n\tds_read_u16 %1, %17 offset:512\n\t"
+        "ds_read_u16 %2, %17 offset:1024\n\tds_read_u16 %3, %17 offset:1536\n\t"
+        "ds_read_u16 %4, %17 offset:2048\n\tds_read_u16 %5, %17 offset:2560\n\t"
+        "ds_read_u16 %6, %17 offset:3072\n\tds_read_u16 %7, %17 offset:3584\n\t"
+        "ds_read_u16 %8, %17 offset:4096\n\tds_read_u16 %9, %17 offset:4608\n\t"
+        "ds_read_u16 %10, %17 offset:5120\n\tds_read_u16 %11, %17 offset:5632\n\t"
+        "ds_read_u16 %12, %17 offset:6144\n\tds_read_u16 %13, %17 offset:6656\n\t"
+        "ds_read_u16 %14, %17 offset:7168\n\tds_read_u16 %15, %17 offset:7680\n\t"
+        "ds_read_b32 %16, %18\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
+          "=&v"(kr[7]), "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
+          "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(wbits)
+        : "v"(la), "v"(lw));
+    const float wl = __uint_as_float(wbits) * kL2e;
+#pragma unroll
+    for (int r = 0; r < kRowsL; ++r) {
+      if (t_hi - 1 - ((int64_t)gi * kRowsL + r) < t_lo) break;   // uniform
+      const float kv = __uint_as_float(kr[r] << 16);
+      const float vv = __uint_as_float(vr[r] << 16);
+      const float e = kv * kL2e - d;
+      float f1, f2;   // 2^(p - p'), 2^(e - p') with p' = max(p, e)
+      pair_scale(s.p, e, f1, f2);
+      s.a = fmaf(f1, s.a, f2 * vv);
+      s.b = fmaf(f1, s.b, f2);
+      s.p = fmaxf(s.p, e);
+      d += wl;
+    }
+  }
+  if (c < p.C) {
+    float* o = p.summ + ((int64_t)b * p.G + g) * 3 * p.C + c;
+    o[0] = s.a;
+    o[p.C] = s.b;
+    o[2 * p.C] = s.p;
+  }
+}
+
 // State entering each segment: s_0 = 0, s_{g+1} = s_g decayed by e^{-w L_g} plus summary g.
 __global__ __launch_bounds__(NT4) void wkv4_carry_kernel(P4 p) {
   const int64_t c = (int64_t)blockIdx.y * NT4 + threadIdx.x;
@@ -280,7 +390,9 @@ hipError_t enqueue_wkv4(const Wkv4Args& a, void* workspace, hipStream_t s) {
   hipError_t e;
   if (pl.G > 1) {
     const dim3 grid((unsigned)(a.B * pl.G), cb);
-    if (a.bf16)
+    if (a.bf16 && a.C % 8 == 0)
+      hipLaunchKernelGGL(wkv4_summary_lds_kernel, grid, block, 0, s, p);
+    else if (a.bf16)
       hipLaunchKernelGGL(wkv4_summary_kernel<true>, grid, block, 0, s, p);
     else
       hipLaunchKernelGGL(wkv4_summary_kernel<false>, grid, block, 0, s, p);

@@ -161,6 +161,21 @@ def test_wkv4_odd_channel_count_segmented(torch_cuda):
     assert e <= TOL4
 
 
+@pytest.mark.parametrize("G", [None, 1, 2, 7, 64])
+def test_wkv4_segments_staged_summaries(torch_cuda, monkeypatch, G):
+    """bf16 with C a multiple of 8: the segment summaries stage k and v
+    through LDS.  C = 264 leaves 8 live channels in the second block of 256;
+    T = 4097 in 64 segments of 65 tokens leaves a last segment of 2 (a single
+    staged group, so the groups read ahead lie past its end)."""
+    if G is not None:
+        monkeypatch.setenv("WKV4_SEGMENTS", str(G))
+    x = I.random_inputs_wkv4(2, 4097, 264, seed=622, dtype="bf16", kscale=2.0)
+    y = run4(x, "bf16")
+    e = err_over_rms(y, wkv4_ref(x["k"], x["v"], x["w"], x["u"]))
+    say(f"[wkv4] B=2 T=4097 C=264 bf16 segments={G}: {e:.3e}")
+    assert e <= TOL4
+
+
 def test_wkv4_empty(torch_cuda):
     torch = torch_cuda
     from linear_attention_rnn_amd import wkv6
