@@ -303,25 +303,44 @@ __global__ __launch_bounds__(NT4) void wkv4_summary_lds_kernel(P4 p) {
 }
 
 // State entering each segment: s_0 = 0, s_{g+1} = s_g decayed by e^{-w L_g} plus summary g.
+// The summaries are loaded kCarryGrp at a time, all before the group's
+// stores (written in the loop, the next summary's loads waited behind the
+// previous entering state's stores: the two regions could alias as far as
+// the compiler knew); slots past the last segment re-read it and are skipped.
+constexpr int kCarryGrp = 8;
+
 __global__ __launch_bounds__(NT4) void wkv4_carry_kernel(P4 p) {
   const int64_t c = (int64_t)blockIdx.y * NT4 + threadIdx.x;
   const int b = blockIdx.x;
   if (c >= p.C) return;
   const float wl = p.w[c] * kL2e;
   St s{0.f, 0.f, -INFINITY};
-  for (int g = 0; g < p.G; ++g) {
-    const int64_t off = ((int64_t)b * p.G + g) * 3 * p.C + c;
-    p.carry[off] = s.a;
-    p.carry[off + p.C] = s.b;
-    p.carry[off + 2 * p.C] = s.p;
-    const float A = p.summ[off], Bs = p.summ[off + p.C], P = p.summ[off + 2 * p.C];
-    const int64_t L = min(p.SEGL, p.T - g * p.SEGL);
-    const float pd = s.p - wl * (float)L;
-    const float p2 = fmaxf(pd, P);
-    const float f1 = e2(pd - p2), f2 = e2(P - p2);
-    s.a = fmaf(f1, s.a, f2 * A);
-    s.b = fmaf(f1, s.b, f2 * Bs);
-    s.p = p2;
+  for (int g0 = 0; g0 < p.G; g0 += kCarryGrp) {
+    float A[kCarryGrp], Bs[kCarryGrp], P[kCarryGrp];
+#pragma unroll
+    for (int u = 0; u < kCarryGrp; ++u) {
+      const int g = min(g0 + u, p.G - 1);
+      const int64_t off = ((int64_t)b * p.G + g) * 3 * p.C + c;
+      A[u] = p.summ[off];
+      Bs[u] = p.summ[off + p.C];
+      P[u] = p.summ[off + 2 * p.C];
+    }
+#pragma unroll
+    for (int u = 0; u < kCarryGrp; ++u) {
+      const int g = g0 + u;
+      if (g >= p.G) break;   // uniform
+      const int64_t off = ((int64_t)b * p.G + g) * 3 * p.C + c;
+      p.carry[off] = s.a;
+      p.carry[off + p.C] = s.b;
+      p.carry[off + 2 * p.C] = s.p;
+      const int64_t L = min(p.SEGL, p.T - g * p.SEGL);
+      const float pd = s.p - wl * (float)L;
+      const float p2 = fmaxf(pd, P[u]);
+      const float f1 = e2(pd - p2), f2 = e2(P[u] - p2);
+      s.a = fmaf(f1, s.a, f2 * A[u]);
+      s.b = fmaf(f1, s.b, f2 * Bs[u]);
+      s.p = p2;
+    }
   }
 }
 
