@@ -244,9 +244,11 @@ __global__ __launch_bounds__(NT4) void wkv4_summary_lds_kernel(P4 p) {
   float d = 0.f;
   for (int gi = 0; gi < ngr; ++gi) {
     // this wave's two loads of group gi are done once at most those of the
-    // groups issued after it remain (loads complete in order; near the end,
-    // where fewer were issued after it than the count allows for, the wait
-    // is only longer than needed)
+    // groups issued after it remain: on gfx9 the vector-memory counter of a
+    // wave's loads drains in issue order (the compiler's own vmcnt(N) waits
+    // between loads rely on the same), and the loop issues no stores.  Near
+    // the end, where fewer were issued after it than the count allows for,
+    // the wait is only longer than needed.
     const int later = min(ngr - 1 - gi, kSlotsL - 2);
     if (later >= 2)
       asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
