@@ -55,12 +55,15 @@ struct P4 {
 
 __device__ __forceinline__ float e2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <bool BF16>
+template <bool BF16, bool NT = false>
 __device__ __forceinline__ float ld(const void* p, int64_t i) {
-  if constexpr (BF16)
-    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
-  else
-    return static_cast<const float*>(p)[i];
+  if constexpr (BF16) {
+    const uint16_t* q = static_cast<const uint16_t*>(p) + i;
+    return __uint_as_float((uint32_t)(NT ? __builtin_nontemporal_load(q) : *q) << 16);
+  } else {
+    const float* q = static_cast<const float*>(p) + i;
+    return NT ? __builtin_nontemporal_load(q) : *q;
+  }
 }
 
 struct St {
@@ -106,8 +109,8 @@ __device__ __forceinline__ void run(const P4& p, St& s, int b, int64_t c, int64_
 #pragma unroll
     for (int j = 0; j < U4; ++j) {
       const int64_t t = t0 + j < t_hi ? t0 + j : t_hi - 1;   // past the end: repeat the last token (unused)
-      kk[j] = ld<BF16>(p.k, base + t * p.C);
-      vv[j] = ld<BF16>(p.v, base + t * p.C);
+      kk[j] = ld<BF16, OUT>(p.k, base + t * p.C);   // the output pass reads them last
+      vv[j] = ld<BF16, OUT>(p.v, base + t * p.C);
     }
   };
   load(t_lo, kc, vc);
