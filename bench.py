@@ -242,7 +242,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; run with --gpus 1", file=sys.stderr)
+        print("bench.py: the library and this benchmark run on one GPU only (no multi-GPU path); run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
