@@ -1097,12 +1097,22 @@ __device__ __forceinline__ bool run_item(const Params& p, char* lds, int bh, int
   return sweep<BF16, false, kOut, CARRY, SLOW, WS, EPI>(p, lds, bh, seg);
 }
 
+// float32 sweeps run at the fix-up kernel's occupancy (two workgroups per
+// CU) already, and with the general sweeps inside they still fit its register
+// budget without spills (resource report, gfx950): they carry them and need
+// no fix-up launch.  bf16 sweeps keep the split (three workgroups per CU).
+template <bool BF16>
+constexpr bool inline_slow() {
+  return !BF16;
+}
+
 template <bool BF16, bool BIDIR, bool CARRY, bool WS, bool EPI>
 __global__ __launch_bounds__(NT, occupancy<BF16>()) void wkv_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[EPI ? SweepLds<BF16>::kBytesEpi : SweepLds<BF16>::kBytes];
   const int bh = CARRY ? blockIdx.x / p.G : blockIdx.x, seg = CARRY ? blockIdx.x % p.G : 0;
   if (EPI && threadIdx.x == 0) *item_marker<EPI>(p, bh, seg) = 0.f;   // clear a marker left by an earlier call
-  if (!run_item<BF16, BIDIR, CARRY, false, WS, EPI>(p, lds, bh, seg)) set_marker(item_marker<EPI>(p, bh, seg));
+  if (!run_item<BF16, BIDIR, CARRY, inline_slow<BF16>(), WS, EPI>(p, lds, bh, seg))
+    set_marker(item_marker<EPI>(p, bh, seg));
 }
 
 template <bool BF16, bool BIDIR, bool CARRY, bool WS, bool EPI>
@@ -1693,14 +1703,15 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 grid(bh * pl.G);
+  constexpr bool kSplit = !inline_slow<BF16>();   // a fix-up launch follows
   if (pl.G > 1) {
     hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true, WS, EPI>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, true, WS, EPI>), grid, block, 0, s, p);
+    if constexpr (kSplit) hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, true, WS, EPI>), grid, block, 0, s, p);
   } else {
     hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false, WS, EPI>), grid, block, 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, false, WS, EPI>), grid, block, 0, s, p);
+    if constexpr (kSplit) hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, false, WS, EPI>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
