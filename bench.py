@@ -10,9 +10,10 @@ Infinity Cache left by the previous steps.
 Prints ONE JSON line (rank 0) with, besides the throughput:
   roofline      achieved HBM bandwidth of the call from HIP events on the launch
                 stream: algorithmic bytes per call / mean call time (the call is
-                the fast-path sweep kernel plus a fix-up kernel that finds no
-                work unless a chunk needed the slow path, plus the segment
-                summary kernels when a sequence is split); traffic = bytes the
+                the sweep kernel, for bf16 inputs the fast-path sweep plus a
+                fix-up kernel that finds no work unless a chunk needed the slow
+                path, plus the segment summary kernels when a sequence is
+                split); traffic = bytes the
                 committed rocprofv3 counter runs measured for the same sources
   mfma          executed matrix-core work per call and its rate vs the bf16 peak
   cpu_baseline  the float64 CPU oracle timed on the host on a bounded sample
@@ -368,10 +369,14 @@ def main() -> int:
                         "mean_call_ms": mean_ms, "algorithmic_flops": flops,
                         "hbm_achieved_GBps": achieved, "algorithmic_bytes": alg_bytes}
     else:
-        kern = {"wkv6_fwd": "wkv6_fwd call: fast-path sweep kernel + fix-up kernel",
-                "wkv6_fwd_gn": "wkv6_fwd_gn call: fast-path sweep kernel with the fused epilogue + fix-up kernel",
+        # bf16 sweeps run the fast path and leave slow chunks to a fix-up
+        # launch; float32 sweeps carry the general sweeps themselves
+        sweep = "fast-path sweep kernel" if w.dtype == "bf16" else "sweep kernel"
+        fix = " + fix-up kernel" if w.dtype == "bf16" else ""
+        kern = {"wkv6_fwd": f"wkv6_fwd call: {sweep}{fix}",
+                "wkv6_fwd_gn": f"wkv6_fwd_gn call: {sweep} with the fused epilogue{fix}",
                 "wkv6_fwd_then_gn": "wkv6_fwd call, then wkv6_group_norm_gate on its y (the unfused order)",
-                "wkv5_fwd": "wkv5_fwd call: fast-path sweep kernel + fix-up kernel",
+                "wkv5_fwd": f"wkv5_fwd call: {sweep}{fix}",
                 "wkv4_fwd": "wkv4_fwd call: per-channel recurrence kernels"}[op]
         if forward6 and plan_segments(w)[0] > 1:
             kern += " + segment summary kernels"
