@@ -86,10 +86,12 @@ def test_gn_parity(torch_cuda, T, mode, dtype):
     check(f"T={T} {mode} {dtype}", x, g, gamma, beta, H, mode, dtype, out)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["causal", "bidirectional"])
-def test_gn_segments_and_slow_path(torch_cuda, monkeypatch, mode):
+def test_gn_segments_and_slow_path(torch_cuda, monkeypatch, mode, dtype):
     """Sequences cut into segments (carries), and decays fast enough that
-    chunks take the general path (the fix-up kernel and its markers)."""
+    chunks take the general path: in the float32 sweeps themselves, for bf16
+    through the fix-up kernel and its markers."""
     B, H, T = 1, 2, 64 * 7 + 9
     C = 64 * H
     for G, slow in ((3, False), (None, True), (4, True)):
@@ -97,27 +99,29 @@ def test_gn_segments_and_slow_path(torch_cuda, monkeypatch, mode):
             monkeypatch.delenv("WKV6_SEGMENTS", raising=False)
         else:
             monkeypatch.setenv("WKV6_SEGMENTS", str(G))
-        x = I.random_inputs(B, T, C, H, seed=720, dtype="f32")
+        x = I.random_inputs(B, T, C, H, seed=720, dtype=dtype)
         if slow:
             x["w_raw"] = np.random.default_rng(721).choice(np.array([-9.0, -0.5, 1.0, 1.5], np.float32),
                                                            size=x["w_raw"].shape)
-        g, gamma, beta = extras(B, T, C, 722, "f32")
-        out = run_gn(x, g, gamma, beta, H, mode, "f32")
-        check(f"segments {G} slow {slow} {mode}", x, g, gamma, beta, H, mode, "f32", out)
+        g, gamma, beta = extras(B, T, C, 722, dtype)
+        out = run_gn(x, g, gamma, beta, H, mode, dtype)
+        check(f"segments {G} slow {slow} {mode} {dtype}", x, g, gamma, beta, H, mode, dtype, out)
 
 
-def test_gn_repeated_calls_reuse_clean_markers(torch_cuda):
-    """A call whose items took the fix-up path, then one that did not, on
-    workspace memory the allocator hands back: the second is still right."""
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gn_repeated_calls_reuse_clean_markers(torch_cuda, dtype):
+    """A call with chunks on the general path (bf16: the fix-up path and its
+    markers), then one without, on workspace memory the allocator hands
+    back: the second is still right."""
     B, H, T = 2, 2, 200
     C = 64 * H
-    x = I.random_inputs(B, T, C, H, seed=730, dtype="f32")
+    x = I.random_inputs(B, T, C, H, seed=730, dtype=dtype)
     x["w_raw"][:, 100:110] = 1.5
-    g, gamma, beta = extras(B, T, C, 731, "f32")
-    check("slow call", x, g, gamma, beta, H, "bidirectional", "f32", run_gn(x, g, gamma, beta, H, "bidirectional", "f32"))
-    x2 = I.random_inputs(B, T, C, H, seed=732, dtype="f32")
-    check("fast call after", x2, g, gamma, beta, H, "bidirectional", "f32",
-          run_gn(x2, g, gamma, beta, H, "bidirectional", "f32"))
+    g, gamma, beta = extras(B, T, C, 731, dtype)
+    check("slow call", x, g, gamma, beta, H, "bidirectional", dtype, run_gn(x, g, gamma, beta, H, "bidirectional", dtype))
+    x2 = I.random_inputs(B, T, C, H, seed=732, dtype=dtype)
+    check("fast call after", x2, g, gamma, beta, H, "bidirectional", dtype,
+          run_gn(x2, g, gamma, beta, H, "bidirectional", dtype))
 
 
 def test_gn_image_base_shape_full(torch_cuda):

@@ -194,17 +194,19 @@ def test_state_in_without_state_out(torch_cuda):
     assert err_over_rms(y, y_ref) <= TOL["f32"]
 
 
-def test_state_through_the_slow_path(torch_cuda):
-    """Decays fast enough that chunks take the general path (the fix-up
-    recomputation) must also start from the given state and hand it back."""
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_through_the_slow_path(torch_cuda, dtype):
+    """Decays fast enough that chunks take the general path (float32: in the
+    sweep itself; bf16: the fix-up recomputation) must also start from the
+    given state and hand it back."""
     B, H, T = 2, 2, 200
-    x = I.random_inputs(B, T, 64 * H, H, seed=52, dtype="f32")
+    x = I.random_inputs(B, T, 64 * H, H, seed=52, dtype=dtype)
     rng = np.random.default_rng(53)
     x["w_raw"] = rng.choice(np.array([-9.0, -0.5, 1.0, 1.5], np.float32), size=x["w_raw"].shape)
     S0 = state_of(B, H, 54)
-    y, S = run_state(x, H, "f32", S0)
+    y, S = run_state(x, H, dtype, S0)
     y_ref, S_ref = ref_state(x, H, S0)
-    check("slow path f32", y, S, y_ref, S_ref, "f32")
+    check(f"slow path {dtype}", y, S, y_ref, S_ref, dtype)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
