@@ -363,6 +363,99 @@ __global__ __launch_bounds__(NT4) void wkv4_out_kernel(P4 p) {
   run<BF16, true>(p, s, b, c, t_lo, t_hi, p.w[c] * kL2e, p.u[c] * kL2e);
 }
 
+// The output pass for bf16 inputs with C a multiple of 8, its k and v rows
+// staged through LDS like the summaries' (same groups, slots and pieces),
+// by workgroups of two roles: four loader waves issue the direct-to-LDS
+// loads and wait for them, four compute waves read the staged rows, run the
+// recurrence and store y.  The vector-memory counter is per wave, so the
+// loader waves' waits count their loads alone, never the compute waves' y
+// stores.  Both roles pass the same one barrier per group.
+__global__ __launch_bounds__(2 * NT4) void wkv4_out_lds_kernel(P4 p) {
+  __shared__ __attribute__((aligned(16))) char tiles[kSlotsL][2][kRowsL * NT4 * 2];
+  const bool loader = threadIdx.x >= NT4;   // uniform per wave
+  const int ct = loader ? threadIdx.x - NT4 : threadIdx.x;   // the thread's channel in the block
+  const int wv = __builtin_amdgcn_readfirstlane(ct >> 6);
+  const int64_t c0 = (int64_t)blockIdx.y * NT4, c = c0 + ct;
+  const int b = blockIdx.x / p.G, g = blockIdx.x % p.G;
+  const int64_t t_lo = g * p.SEGL, t_hi = min(p.T, t_lo + p.SEGL);
+  const int ngr = (int)((t_hi - t_lo + kRowsL - 1) / kRowsL);
+  // loader: this thread's piece of a group tile (row ct / 32, channels 8 (ct % 32)..)
+  const int prow = ct >> 5;
+  const int64_t pch = c0 + 8 * (ct & 31);
+  const int64_t rowb = p.C * 2;
+  const int64_t off0 = ((int64_t)b * p.T * p.C + (pch < p.C ? pch : c0)) * 2;
+  const char* kb = static_cast<const char*>(p.k) + off0;
+  const char* vb = static_cast<const char*>(p.v) + off0;
+  // group gi: tokens t_lo + gi kRowsL + r, r = 0..; rows past the segment re-read its last token
+  auto issue = [&](int gi) {
+    int64_t t = t_lo + (int64_t)gi * kRowsL + prow;
+    if (t >= t_hi) t = t_hi - 1;
+    __builtin_amdgcn_global_load_lds(kb + t * rowb, (lds_void*)(tiles[gi % kSlotsL][0] + wv * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + t * rowb, (lds_void*)(tiles[gi % kSlotsL][1] + wv * 1024), 16, 0, 0);
+  };
+  // compute: the channel's state, decay and bonus (loaded, and waited for,
+  // before the loop)
+  const int64_t cc = c < p.C ? c : c0;
+  St s{0.f, 0.f, -INFINITY};
+  float wl = 0.f, ul = 0.f;
+  if (loader) {
+#pragma unroll
+    for (int gi = 0; gi < kSlotsL - 1; ++gi) issue(gi);
+  } else {
+    if (p.G > 1) {
+      const float* ci = p.carry + ((int64_t)b * p.G + g) * 3 * p.C + cc;
+      s = St{ci[0], ci[p.C], ci[2 * p.C]};
+    }
+    wl = p.w[cc] * kL2e;
+    ul = p.u[cc] * kL2e;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  float* yp = p.y + (int64_t)b * p.T * p.C + c;
+  for (int gi = 0; gi < ngr; ++gi) {
+    if (loader) {
+      // this wave's loads of group gi are done once at most those of the
+      // groups issued after it remain (in issue order: the wave issues no
+      // other vector-memory operation in the loop)
+      const int later = min(ngr - 1 - gi, kSlotsL - 2);
+      if (later >= 2)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    lds_barrier4();   // group gi has landed; group gi - 1's slot is free
+    if (loader) {
+      if (gi + kSlotsL - 1 < ngr) issue(gi + kSlotsL - 1);
+      continue;
+    }
+    // the group's rows, read in one asm block that waits for its own reads
+    const uint32_t la = (uint32_t)(uintptr_t)(lds_char*)(tiles[gi % kSlotsL][0]) + 2u * (uint32_t)ct;
+    uint32_t kr[kRowsL], vr[kRowsL];
+    asm volatile(
+        "ds_read_u16 %0, %16\n\tds_read_u16 %1, %16 offset:512\n\t"
+        "ds_read_u16 %2, %16 offset:1024\n\tds_read_u16 %3, %16 offset:1536\n\t"
+        "ds_read_u16 %4, %16 offset:2048\n\tds_read_u16 %5, %16 offset:2560\n\t"
+        "ds_read_u16 %6, %16 offset:3072\n\tds_read_u16 %7, %16 offset:3584\n\t"
+        "ds_read_u16 %8, %16 offset:4096\n\tds_read_u16 %9, %16 offset:4608\n\t"
+        "ds_read_u16 %10, %16 offset:5120\n\tds_read_u16 %11, %16 offset:5632\n\t"
+        "ds_read_u16 %12, %16 offset:6144\n\tds_read_u16 %13, %16 offset:6656\n\t"
+        "ds_read_u16 %14, %16 offset:7168\n\tds_read_u16 %15, %16 offset:7680\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
+          "=&v"(kr[7]), "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
+          "=&v"(vr[6]), "=&v"(vr[7])
+        : "v"(la));
+#pragma unroll
+    for (int r = 0; r < kRowsL; ++r) {
+      const int64_t t = t_lo + (int64_t)gi * kRowsL + r;
+      if (t >= t_hi) break;   // uniform
+      const float y = step<true>(s, __uint_as_float(kr[r] << 16), __uint_as_float(vr[r] << 16), wl, ul);
+      if (c < p.C) __builtin_nontemporal_store(y, yp + t * p.C);   // not read again
+    }
+  }
+}
+
 struct Plan4 {
   int G;
   int64_t SEGL;
@@ -425,7 +518,9 @@ hipError_t enqueue_wkv4(const Wkv4Args& a, void* workspace, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(a.B * pl.G), cb);
-  if (a.bf16)
+  if (a.bf16 && a.C % 8 == 0)
+    hipLaunchKernelGGL(wkv4_out_lds_kernel, grid, dim3(2 * NT4), 0, s, p);
+  else if (a.bf16)
     hipLaunchKernelGGL(wkv4_out_kernel<true>, grid, block, 0, s, p);
   else
     hipLaunchKernelGGL(wkv4_out_kernel<false>, grid, block, 0, s, p);
