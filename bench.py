@@ -92,6 +92,13 @@ def plan_segments(w: I.Workload) -> tuple[int, int]:
     else:
         target = 256 * (3 if w.dtype == "bf16" else 2)
         g = math.ceil(target / bh) if bh < target else 1
+        if w.dtype == "bf16" and bh < target:
+            # the library prefers a grid with as many workgroups on every CU
+            for per in (3, 2):
+                want = 256 * per
+                if want % bh == 0 and want // bh <= nc and math.ceil(nc / math.ceil(nc / (want // bh))) == want // bh:
+                    g = want // bh
+                    break
     g = max(1, min(g, nc))
     segc = math.ceil(nc / g)
     return math.ceil(nc / segc), segc

@@ -1632,6 +1632,27 @@ Plan plan(const FwdArgs& a) {
     // enough workgroups to fill every CU at the kernel's occupancy
     const int64_t target = 256 * (a.bf16 ? 3 : 2);
     if (bh < target) G = (int)((target + bh - 1) / bh);
+    // bf16: a grid that gives every CU the same number of workgroups, three
+    // or else two, wins over a fuller but uneven one (segments are whole
+    // chunks, so the count above can round to, say, 704 workgroups: two on
+    // some CUs, three on others).  Measured at T = 4096: 64 pairs in 8
+    // segments against 11 (bidirectional 153.6 against 158.2 us, causal 88.8
+    // against 90.5), 32 pairs in 16 against 22 (86.6 against 100.7, 58.8
+    // against 67.2); 128 pairs stay at 6 segments (768 workgroups), which
+    // beat 4 (281 against 296 us).
+    if (a.bf16 && bh < target) {
+      for (int per = 3; per >= 2; --per) {
+        const int64_t want = 256 * per;
+        if (want % bh != 0) continue;
+        const int64_t g0 = want / bh;
+        if (g0 > pl.NC) continue;
+        const int64_t segc = (pl.NC + g0 - 1) / g0;
+        if ((pl.NC + segc - 1) / segc == g0) {
+          G = (int)g0;
+          break;
+        }
+      }
+    }
   }
   G = max(1, min(G, pl.NC));
   pl.SEGC = (pl.NC + G - 1) / G;

@@ -322,6 +322,30 @@ def test_fwd_workspace_bytes_follows_the_documented_formula():
         assert 1 < G <= (T + 63) // 64, (B, T, G)
 
 
+def test_segment_plan_prefers_grids_even_over_the_cus():
+    """The forward's segment count (read back from the workspace size, host
+    arithmetic): for bf16 calls it picks a grid with three, else two,
+    workgroups on every one of the 256 CUs when whole chunks allow it (the
+    measured shapes), and bench.py's mirror of the planner agrees with the
+    library on every benchmark workload."""
+    import bench
+    from linear_attention_rnn_amd import inputs as I
+
+    per = 2 * (64 * 64 + 64) * 4
+
+    def segments(B, T, H, mode, bf16):
+        n = wkv6.fwd_workspace_bytes(B, T, 64 * H, H, mode, bf16)
+        return n // (B * H * per) if n else 1
+
+    assert segments(4, 4096, 16, "bidirectional", True) == 8      # 64 pairs: 512 workgroups, not 704
+    assert segments(2, 4096, 16, "bidirectional", True) == 16     # 32 pairs: 512, not 704
+    assert segments(2, 4096, 32, "causal", True) == 8
+    assert segments(8, 4096, 16, "bidirectional", True) == 6      # 128 pairs: 768
+    assert segments(8, 4096, 32, "causal", True) == 3             # 256 pairs: 768
+    for w in I.WORKLOADS:
+        assert segments(w.B, w.T, w.H, w.mode, w.dtype == "bf16") == bench.plan_segments(w)[0], w.name
+
+
 def test_workspace_keep_bound_matches_the_header():
     import re
 
