@@ -1106,8 +1106,11 @@ constexpr bool inline_slow() {
   return !BF16;
 }
 
-template <bool BF16, bool BIDIR, bool CARRY, bool WS, bool EPI>
-__global__ __launch_bounds__(NT, occupancy<BF16>()) void wkv_kernel(Params p) {
+// OCC: workgroups per CU the registers are allocated for.  A bf16
+// bidirectional grid of at most two workgroups per CU runs a variant
+// allocated for two: 192 VGPRs and no spills, where three per CU spill.
+template <bool BF16, bool BIDIR, bool CARRY, bool WS, bool EPI, int OCC = occupancy<BF16>()>
+__global__ __launch_bounds__(NT, OCC) void wkv_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[EPI ? SweepLds<BF16>::kBytesEpi : SweepLds<BF16>::kBytes];
   const int bh = CARRY ? blockIdx.x / p.G : blockIdx.x, seg = CARRY ? blockIdx.x % p.G : 0;
   if (EPI && threadIdx.x == 0) *item_marker<EPI>(p, bh, seg) = 0.f;   // clear a marker left by an earlier call
@@ -1725,12 +1728,30 @@ hipError_t launch_t(const FwdArgs& a, const Plan& pl, void* ws, hipStream_t s) {
   }
   const dim3 grid(bh * pl.G);
   constexpr bool kSplit = !inline_slow<BF16>();   // a fix-up launch follows
+  // a bf16 bidirectional grid of at most two workgroups per CU: the variant
+  // with their registers (the causal sweeps fit three per CU unspilled)
+  constexpr bool kTwo = BF16 && BIDIR && !EPI;
+  const bool two = kTwo && grid.x <= 2u * 256u;
   if (pl.G > 1) {
-    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true, WS, EPI>), grid, block, 0, s, p);
+    if constexpr (kTwo) {
+      if (two)
+        hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true, WS, EPI, 2>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true, WS, EPI>), grid, block, 0, s, p);
+    } else {
+      hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, true, WS, EPI>), grid, block, 0, s, p);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if constexpr (kSplit) hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, true, WS, EPI>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false, WS, EPI>), grid, block, 0, s, p);
+    if constexpr (kTwo) {
+      if (two)
+        hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false, WS, EPI, 2>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false, WS, EPI>), grid, block, 0, s, p);
+    } else {
+      hipLaunchKernelGGL((wkv_kernel<BF16, BIDIR, false, WS, EPI>), grid, block, 0, s, p);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if constexpr (kSplit) hipLaunchKernelGGL((wkv_fixup_kernel<BF16, BIDIR, false, WS, EPI>), grid, block, 0, s, p);
   }
