@@ -653,7 +653,9 @@ __device__ __forceinline__ void progress_priority(int done, int total) {
 // EPI: the sweep that produces the final outputs (the causal sweep, or the
 // forward sweep of a bidirectional call) writes them through the fused
 // GroupNorm / gate epilogue as bf16 instead of writing y.
-template <bool BF16, bool REV, int MODE, bool CARRY, bool SLOW, bool WS = false, bool EPI = false>
+// OCC only tells apart the instantiations of kernels allocated for
+// different occupancies, so that each has its own copy of the sweep.
+template <bool BF16, bool REV, int MODE, bool CARRY, bool SLOW, bool WS = false, bool EPI = false, int OCC = 0>
 __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int seg, int npass = 1,
                                       int pass = 0) {
   constexpr int SP = BF16 ? 2 : 3;
@@ -1084,17 +1086,17 @@ __device__ __forceinline__ bool marker_set(const float* m) {
 
 // Outputs of one item with the sweeps on the fast path (SLOW = false: false
 // as soon as a chunk needs the slow path) or the general sweeps.
-template <bool BF16, bool BIDIR, bool CARRY, bool SLOW, bool WS, bool EPI>
+template <bool BF16, bool BIDIR, bool CARRY, bool SLOW, bool WS, bool EPI, int OCC = 0>
 __device__ __forceinline__ bool run_item(const Params& p, char* lds, int bh, int seg) {
   if (BIDIR) {
     // the forward sweep runs even after the reverse one gave up (its result is
     // then recomputed anyway): one straight path keeps the registers of the
     // two sweeps apart
-    const bool ok = sweep<BF16, true, kOut, CARRY, SLOW, WS, EPI>(p, lds, bh, seg, 2, 0);
+    const bool ok = sweep<BF16, true, kOut, CARRY, SLOW, WS, EPI, OCC>(p, lds, bh, seg, 2, 0);
     __syncthreads();   // partial rows of y written; LDS free for reuse
-    return sweep<BF16, false, kOutAcc, CARRY, SLOW, WS, EPI>(p, lds, bh, seg, 2, 1) && ok;
+    return sweep<BF16, false, kOutAcc, CARRY, SLOW, WS, EPI, OCC>(p, lds, bh, seg, 2, 1) && ok;
   }
-  return sweep<BF16, false, kOut, CARRY, SLOW, WS, EPI>(p, lds, bh, seg);
+  return sweep<BF16, false, kOut, CARRY, SLOW, WS, EPI, OCC>(p, lds, bh, seg);
 }
 
 // float32 sweeps run at the fix-up kernel's occupancy (two workgroups per
@@ -1114,7 +1116,7 @@ __global__ __launch_bounds__(NT, OCC) void wkv_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[EPI ? SweepLds<BF16>::kBytesEpi : SweepLds<BF16>::kBytes];
   const int bh = CARRY ? blockIdx.x / p.G : blockIdx.x, seg = CARRY ? blockIdx.x % p.G : 0;
   if (EPI && threadIdx.x == 0) *item_marker<EPI>(p, bh, seg) = 0.f;   // clear a marker left by an earlier call
-  if (!run_item<BF16, BIDIR, CARRY, inline_slow<BF16>(), WS, EPI>(p, lds, bh, seg))
+  if (!run_item<BF16, BIDIR, CARRY, inline_slow<BF16>(), WS, EPI, OCC>(p, lds, bh, seg))
     set_marker(item_marker<EPI>(p, bh, seg));
 }
 
