@@ -1052,13 +1052,14 @@ __device__ __forceinline__ bool sweep(const Params& p, char* lds, int bh, int se
 // forward sweep (it adds its part to y) in the same workgroup, so the partial
 // rows are read back from the L2 of the same XCD.
 //
-// Every item first runs with the fast path alone (wkv_kernel),
+// bf16 items first run with the fast path alone (wkv_kernel),
 // register-allocated for three resident workgroups per CU.  A workgroup that
 // meets a chunk needing the slow path stops and leaves a marker in the first
 // word of its output (y at the segment's first token and the head's first
 // channel); the fix-up kernel launched next recomputes exactly the marked
 // items with the general sweeps, which need more registers than the fast
-// kernel has.  (The summary kernels need no such split: see there.)
+// kernel has.  float32 sweeps carry the general sweeps themselves (see
+// inline_slow).  (The summary kernels need no such split: see there.)
 // A marker bit pattern produced by the arithmetic itself (a NaN input that
 // propagates there) only costs a needless recomputation.
 constexpr uint32_t kRedo = 0x7FC0D1A5u;   // quiet NaN with a payload
