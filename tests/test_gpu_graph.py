@@ -6,14 +6,15 @@ replay must equal, bit for bit, the eager call on the same inputs (the same
 kernels on the same data).  Captured: an unsegmented bidirectional forward
 (no workspace), a segmented causal forward through wkv6_fwd_noalloc (its
 workspace is the static scratch array, so nothing is allocated under
-capture), and an 8-step single-token decode loop passing the state between
-two buffers.
+capture), an 8-step single-token decode loop passing the state between
+two buffers, and the RWKV-5 and RWKV-4 forwards on shapes that need no
+workspace.
 """
 import numpy as np
 import pytest
 
 from linear_attention_rnn_amd import inputs as I
-from tests.gpu_util import device_inputs, say
+from tests.gpu_util import device_inputs, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -28,19 +29,19 @@ def torch_cuda():
     return torch
 
 
-def _static(torch, x, dtype):
-    return [t.clone() for t in device_inputs(x, dtype)]
+def _static(torch, x, dtype, dev=device_inputs):
+    return [t.clone() for t in dev(x, dtype)]
 
 
-def _refill(static, x, dtype):
-    for dst, src in zip(static, device_inputs(x, dtype)):
+def _refill(static, x, dtype, dev=device_inputs):
+    for dst, src in zip(static, dev(x, dtype)):
         dst.copy_(src)
 
 
-def _replay_and_compare(torch, graph, static, out, eager, draw, dtype, label):
+def _replay_and_compare(torch, graph, static, out, eager, draw, dtype, label, dev=device_inputs):
     for rep in range(REPLAYS):
         x = draw(rep)
-        _refill(static, x, dtype)          # eager work between replays
+        _refill(static, x, dtype, dev)     # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -148,3 +149,51 @@ def test_decode_loop_under_capture(torch_cuda):
         for a, b in zip(got, want):
             assert torch.equal(a, b), f"decode loop: replay {rep} differs from the eager loop"
         say(f"[graph] decode loop: replay {rep} equals the eager loop")
+
+
+@pytest.mark.parametrize("mode", ["causal", "bidirectional"])
+def test_fwd5_under_capture(torch_cuda, mode):
+    """RWKV-5 (one decay per channel), B*H = 768 items, no workspace."""
+    torch = torch_cuda
+    from linear_attention_rnn_amd import wkv6
+
+    B, T, H = 64, 150, 12
+    C = 64 * H
+    assert wkv6.fwd_workspace_bytes(B, T, C, H, mode, True) == 0
+    draw = lambda rep: I.random_inputs_wkv5(B, T, C, seed=740 + rep, dtype="bf16")
+    static = _static(torch, draw(0), "bf16")
+    y = torch.empty(B, T, C, dtype=torch.float32, device="cuda")
+    wkv6.fwd5(*static, H, mode, out=y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wkv6.fwd5(*static, H, mode, out=y)
+    _replay_and_compare(torch, g, static, [y], lambda s: [wkv6.fwd5(*s, H, mode)], draw, "bf16",
+                        f"fwd5 {mode}")
+
+
+def _dev4(x, dtype):
+    import torch
+
+    return ([to_device(x[key], dtype) for key in ("k", "v")]
+            + [torch.from_numpy(np.ascontiguousarray(x[key], np.float32)).cuda() for key in ("w", "u")])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fwd4_under_capture(torch_cuda, dtype):
+    """RWKV-4 over 196 tokens of 64 x 768 channels: one pass, no segments and
+    so no workspace (bf16 takes the LDS-staged output kernel)."""
+    torch = torch_cuda
+    from linear_attention_rnn_amd import wkv6
+
+    B, T, C = 64, 196, 768
+    draw = lambda rep: I.random_inputs_wkv4(B, T, C, seed=750 + rep, dtype=dtype)
+    static = _static(torch, draw(0), dtype, _dev4)
+    y = torch.empty(B, T, C, dtype=torch.float32, device="cuda")
+    wkv6.fwd4(*static, out=y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wkv6.fwd4(*static, out=y)
+    _replay_and_compare(torch, g, static, [y], lambda s: [wkv6.fwd4(*s)], draw, dtype,
+                        f"fwd4 {dtype}", _dev4)
